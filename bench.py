@@ -1,0 +1,213 @@
+"""Benchmark of one DDTree verify step on one MI355X.
+
+A step is the whole hot path on one batch of synthetic input: one layer of
+tree-verify attention for a budget-22 tree (23 nodes) over a 128K-row Q4_0
+KV cache (24 query / 4 KV heads, head_dim 256, no window), then greedy
+acceptance over 23 x 152000 fp32 logits. Inputs are resident in HBM before
+the timed region; the KV cache rotates over enough copies (>= 1 GiB) that
+the 256 MB Infinity Cache cannot hold it between steps.
+
+Prints one JSON line. `value` is verify steps per second. Extra fields give
+the effective KV bandwidth, the chain-16 comparison, the roofline of the
+attention launch and the CPU oracle's speed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+
+METRIC = "tree-verify steps/s and effective KV GB/s (% HBM peak), budget 22 @128K ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long", choices=["long", "27b", "window"])
+    ap.add_argument("--kv", default="q4_0", choices=["q4_0", "f16"])
+    ap.add_argument("--rotate-bytes", type=float, default=1.1e9, help="KV bytes the copies span at least")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=96, help="oracle output rows timed for the CPU baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tree_verify_attention_ddtree_amd as tv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = dict(synth.WORKLOADS[args.workload])
+    Hq, Hkv, D, T = w["n_q_heads"], w["n_kv_heads"], w["head_dim"], w["n_ctx"]
+    W = w.get("window", 0)
+    vocab = synth.WORKLOADS["full"]["vocab"]
+    kvt = tv.TV_KV_Q4_0 if args.kv == "q4_0" else tv.TV_KV_F16
+
+    inp = synth.attn_inputs(**w, kv=args.kv)
+    parent = inp["parent"]
+    n = len(parent)
+    s = synth.streams(w["seed"])
+    tokens = synth.sibling_distinct_tokens(s["tokens"], parent, vocab)
+    logits, planted_L, _ = synth.planted_logits(s["logits"], parent, tokens, vocab)
+
+    kc0 = torch.from_numpy(inp["k_cache"]).to(dev)
+    vc0 = torch.from_numpy(inp["v_cache"]).to(dev)
+    kv_bytes_alloc = 2 * kc0.numel() * kc0.element_size()
+    n_copies = max(1, int(np.ceil(args.rotate_bytes / kv_bytes_alloc)))
+    caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(n_copies - 1)]
+    q = torch.from_numpy(inp["q"]).to(dev)
+    kt = torch.from_numpy(inp["k_tree"]).to(dev)
+    vt = torch.from_numpy(inp["v_tree"]).to(dev)
+    out = torch.empty((n, Hq, D), dtype=torch.float32, device=dev)
+    ts, hs = tv.cache_strides(kc0, kvt)
+    desc, _par = tv.make_desc(parent, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs)
+    wsb = tv.tv_attn_workspace_bytes(desc)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    lg = torch.from_numpy(logits).to(dev)
+    am = torch.empty(n, dtype=torch.int32, device=dev)
+    res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
+    aws = torch.empty(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # chain-16 comparison (same cache, block-size-16 chain instead of the tree)
+    chain = synth.chain_tree(16)
+    cdesc, _cpar = tv.make_desc(chain, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs)
+    cws = torch.empty(max(tv.tv_attn_workspace_bytes(cdesc), 16), dtype=torch.uint8, device=dev)
+    cq, ckt, cvt = q[:16].contiguous(), kt[:16].contiguous(), vt[:16].contiguous()
+    cout = torch.empty((16, Hq, D), dtype=torch.float32, device=dev)
+
+    def attn(i):
+        kc, vc = caches[i % n_copies]
+        tv.tree_verify_attn(desc, kc, vc, q, kt, vt, out, ws, wsb, stream)
+
+    def accept():
+        tv.tree_accept(lg, parent, tokens, am, res, aws, stream)
+
+    def step(i):
+        attn(i)
+        accept()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(k):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k  # ms per call
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    # per-launch durations of the parts, same stream, same rotation
+    ms_attn = timed(attn, args.steps)
+    ms_accept = timed(lambda i: accept(), args.steps)
+    ms_chain = timed(lambda i: tv.tree_verify_attn(cdesc, caches[i % n_copies][0], caches[i % n_copies][1], cq,
+                                                   ckt, cvt, cout, cws, None, stream), args.steps)
+    assert int(res[0].item()) == planted_L
+
+    # algorithmic work of one attention launch
+    R = T - max(0, T - W) if W > 0 else T
+    row_bytes = (D // 32 * 18) if args.kv == "q4_0" else 2 * D
+    kv_bytes = 2 * Hkv * R * row_bytes
+    flops = 4.0 * Hq * n * R * D
+    kv_gbps = kv_bytes / (ms_attn * 1e-3) / 1e9
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    chain_kv_gbps = kv_bytes / (ms_chain * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": 1e3 / ms_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"one verify step: tree-verify attention (1 layer, {Hq} q / {Hkv} kv heads, head_dim {D}, "
+                         f"ctx {T}, window {W}, {args.kv} KV, budget-22 tree of {n} nodes) + greedy acceptance "
+                         f"over {n}x{vocab} fp32 logits"),
+            "kv": args.kv, "n_ctx": T, "window": W, "n_nodes": n, "vocab": vocab,
+            "kv_copies_rotated": n_copies,
+        },
+        "kv_gbps": kv_gbps,
+        "kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
+        "attn_us": ms_attn * 1e3,
+        "accept_us": ms_accept * 1e3,
+        "chain16_attn_us": ms_chain * 1e3,
+        "chain16_kv_gbps": chain_kv_gbps,
+        "roofline": {
+            "kernel": "tree_verify_attn launch (split kernel + merge kernel)",
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_FP16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops": flops,
+            "algorithmic_kv_bytes": kv_bytes,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, logits, parent, tokens, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, logits, parent, tokens, n_rows):
+    """The oracle (fp64, OpenMP) on a bounded sample of the same step: the
+    first n_rows output rows of the attention, extrapolated to all rows, plus
+    the full acceptance."""
+    import oracle
+    n = len(parent)
+    Hq = inp["n_q_heads"]
+    total = n * Hq
+    k = min(n_rows, total)
+    rows = list(range(k))
+    t0 = time.perf_counter()
+    oracle.attn(inp, rows=rows)
+    t1 = time.perf_counter()
+    oracle.accept(logits, parent, tokens)
+    t2 = time.perf_counter()
+    step_s = (t1 - t0) * total / k + (t2 - t1)
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
+    return {
+        "value": 1.0 / step_s,
+        "unit": "steps/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"attention rows 0..{k - 1} of {total} ({(t1 - t0):.1f} s, scaled by {total / k:.2f}) "
+                  f"+ full acceptance ({(t2 - t1) * 1e3:.0f} ms)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * tree_verify.h -- C ABI of libtv.so: DDTree tree-verify attention and greedy
+ * acceptance on MI355X (gfx950).
+ *
+ * The method (Luce DFlash pages: "Luce DFlash: 単一RTX 3090で最大2倍の
+ * スループットを目指すQwen3.6-27B", feature list; "We got 207 tok/s with
+ * Qwen3.5-27B on an RTX 3090", claims and "What we built vs what we didn't"):
+ * a DFlash draft proposes a DDTree of draft tokens (budget 22, i.e. 23 nodes
+ * with the root, block size 16); the target model scores every node of the
+ * tree in a single verify pass; verification is greedy. The KV cache of the
+ * target is F16 or Q4_0 (the Q4_0 path reaches about 128K context), and decode
+ * may restrict attention to a sliding window of 2048 tokens.
+ *
+ * This library implements the data-parallel core of that verify pass:
+ *   tree_verify_attn  one attention layer of the verify pass: every tree node
+ *                     attends to the committed cache rows (inside the window)
+ *                     and to its own tree ancestors, itself included;
+ *   tree_accept       greedy acceptance: per-node argmax over the vocabulary
+ *                     and the longest root path whose draft tokens match.
+ *
+ * Conventions shared by all calls
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream). Results are valid once the stream has been synchronised.
+ *   - The library allocates no device memory. Inputs, outputs and workspaces
+ *     belong to the caller and must stay alive until the stream reaches them.
+ *   - Host arrays passed in (parent, tokens) are read during the call only.
+ *   - Every argument check runs on the host before anything is launched; on
+ *     an error nothing is launched and no output is written.
+ *   - The library keeps no mutable global state; calls from several threads
+ *     on different streams are safe.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_API __attribute__((visibility("default")))
+
+/* Status codes. */
+#define TV_OK 0
+#define TV_E_ARG (-1)       /* null pointer, bad enum, non-positive scale, ... */
+#define TV_E_TREE (-2)      /* parent array is not a rooted topological tree   */
+#define TV_E_SHAPE (-3)     /* head counts / head_dim / sizes not supported    */
+#define TV_E_ALIGN (-4)     /* pointer or stride misaligned                    */
+#define TV_E_WORKSPACE (-5) /* workspace missing or too small                  */
+#define TV_E_HIP (-6)       /* a HIP runtime call or kernel launch failed      */
+
+/* KV cache storage types. */
+#define TV_KV_F16 0  /* IEEE binary16, one row = head_dim values             */
+#define TV_KV_Q4_0 1 /* ggml Q4_0: per 32 values an 18-byte block = fp16
+                        scale (little endian) + 16 code bytes; element e
+                        (0..15) of a block is the low nibble of code byte e,
+                        element e+16 its high nibble; value = scale*(code-8) */
+
+#define TV_MAX_NODES 64
+
+/*
+ * Shape of one verify-attention layer.
+ *
+ * n_nodes      tree size, 1..TV_MAX_NODES (budget 22 -> 23). Node 0 is the
+ *              root: the last emitted token, whose K/V are not yet in the
+ *              cache.
+ * parent       HOST int32[n_nodes]: parent[0] == -1 and 0 <= parent[i] < i
+ *              (topological numbering); anything else is TV_E_TREE.
+ * n_q_heads    query heads H_q; n_kv_heads H_kv divides it. Query head h
+ *              reads KV head h / (H_q / H_kv).
+ * head_dim     64, 128 or 256.
+ * kv_type      TV_KV_F16 or TV_KV_Q4_0.
+ * n_ctx        committed cache rows (>= 0).
+ * window       0: attend to all rows; W > 0: only to rows
+ *              [max(0, n_ctx - W), n_ctx). The window counts cache rows only;
+ *              every node also sees all of its ancestors.
+ * kv_token_stride  bytes from row j to row j+1 of one KV head (>= row size,
+ *              multiple of 4 for Q4_0 and of 16 for F16).
+ * kv_head_stride   bytes from KV head g to g+1 (multiple of 4 / 16 likewise).
+ *              Head-major caches use token_stride = row bytes and
+ *              head_stride = n_rows_allocated * row bytes.
+ * scale        softmax scale applied to q.k (finite, > 0), usually
+ *              1/sqrt(head_dim).
+ */
+typedef struct tv_attn_desc {
+    int32_t n_nodes;
+    const int32_t *parent;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t kv_type;
+    int64_t n_ctx;
+    int64_t window;
+    int64_t kv_token_stride;
+    int64_t kv_head_stride;
+    float scale;
+} tv_attn_desc;
+
+/*
+ * Device buffers of one layer (all caller-owned, base pointers 16-byte
+ * aligned).
+ *
+ * k_cache, v_cache  the committed cache, laid out by the strides above.
+ *                   May be NULL when n_ctx == 0.
+ * q                 fp16 [n_nodes][n_q_heads][head_dim]
+ * k_tree, v_tree    fp16 [n_nodes][n_kv_heads][head_dim]: K/V of the tree
+ *                   nodes themselves (after any positional encoding).
+ * out               fp32 [n_nodes][n_q_heads][head_dim]
+ */
+typedef struct tv_attn_ptrs {
+    const void *k_cache;
+    const void *v_cache;
+    const void *q;
+    const void *k_tree;
+    const void *v_tree;
+    float *out;
+} tv_attn_ptrs;
+
+/*
+ * Device workspace (bytes) tree_verify_attn needs for `d`: partial softmax
+ * states of the key-range splits. 0 when `d` is invalid or no split is
+ * needed (n_ctx == 0 after the window). Depends on the device's compute-unit
+ * count, so query it for the device the call will run on (the current one).
+ */
+TV_API size_t tv_attn_workspace_bytes(const tv_attn_desc *d);
+
+/*
+ * One layer of tree-verify attention, asynchronous on `stream`:
+ *   out[i][h] = softmax over keys k of scale * q[i][h] . k, applied to the
+ *   matching values, where the keys are the cache rows of the window and the
+ *   tree nodes j that are ancestors of i or i itself.
+ * Computation: fp16 products with fp32 accumulation; probabilities are
+ * rounded to fp16 before they weight the cache values.
+ * `workspace` must hold tv_attn_workspace_bytes(d) bytes (NULL allowed when
+ * that is 0), 16-byte aligned, and is overwritten.
+ * Returns TV_OK or a TV_E_* code (nothing is launched on error).
+ */
+TV_API int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Device workspace (bytes) tree_accept needs for n_nodes x vocab logits. */
+TV_API size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab);
+
+/*
+ * Greedy acceptance of one verify step, asynchronous on `stream`.
+ *
+ * logits      device fp32 [n_nodes][vocab], 16-byte aligned, vocab >= 1.
+ * parent      HOST int32[n_nodes], as in tv_attn_desc.
+ * tokens      HOST int32[n_nodes]: draft token of each node (tokens[0], the
+ *             root's, is not used).
+ * argmax_out  device int32[n_nodes]: a[i] = argmax_v logits[i][v] with -0 ==
+ *             +0, NaN below every number, ties to the smallest v, an all-NaN
+ *             row giving 0.
+ * result_out  device int32[2 + 2*n_nodes]:
+ *               [0] n_acc, the number of accepted draft tokens;
+ *               [1] the bonus token, a[last accepted node];
+ *               [2 .. 2+n) the accepted path, node indices from the root,
+ *                          padded with -1;
+ *               [2+n .. 2+2n) the emitted tokens: tokens of path[1..n_acc],
+ *                          then the bonus token, padded with -1.
+ *             The accepted path is the longest root path along which every
+ *             child's token equals its parent's argmax; among equally long
+ *             ones, the one with the smaller child index where they diverge.
+ * workspace   device, tv_accept_workspace_bytes(n_nodes, vocab) bytes,
+ *             8-byte aligned, overwritten.
+ */
+TV_API int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
+                const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Static string for a status code. */
+TV_API const char *tv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_VERIFY_H */

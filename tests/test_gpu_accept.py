@@ -1,0 +1,89 @@
+"""GPU parity of tree_accept against the CPU oracle: bit-exact argmax,
+accepted path, emitted tokens and bonus token."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import gpu_accept
+
+pytestmark = pytest.mark.gpu
+
+
+def check(logits, parent, tokens):
+    am, res = gpu_accept(logits, parent, tokens)
+    ram, rres = oracle.accept(logits, parent, tokens)
+    assert np.array_equal(am, ram), (am, ram)
+    assert np.array_equal(res, rres), (res, rres)
+    return rres
+
+
+def test_tiny_planted():
+    w = synth.WORKLOADS["tiny"]
+    for seed in range(20):
+        s = synth.streams(seed)
+        parent = synth.draft_tree(s["tree"], 8, 4)
+        tok = synth.sibling_distinct_tokens(s["tokens"], parent, w["vocab"])
+        logits, L, _ = synth.planted_logits(s["logits"], parent, tok, w["vocab"])
+        assert check(logits, parent, tok)[0] == L
+
+
+def test_full_vocab_planted_64_trees():
+    """23 x 152000 logits, planted paths, the 64 trees of the full step."""
+    V = synth.WORKLOADS["full"]["vocab"]
+    for t in range(64):
+        s = synth.streams(5000 + t)
+        parent = synth.draft_tree(s["tree"], 23, 16)
+        tok = synth.sibling_distinct_tokens(s["tokens"], parent, V)
+        logits, L, _ = synth.planted_logits(s["logits"], parent, tok, V)
+        assert check(logits, parent, tok)[0] == L
+
+
+@pytest.mark.parametrize("vocab", [1, 3, 7, 8191, 8192, 8193, 30001, 152000, 152003])
+def test_vocab_sizes(vocab):
+    rng = np.random.default_rng(vocab)
+    parent = synth.draft_tree(rng, 23, 16)
+    tok = rng.integers(0, vocab, size=23).astype(np.int32)
+    logits = rng.standard_normal((23, vocab)).astype(np.float32)
+    check(logits, parent, tok)
+
+
+def test_ties_zeros_nan():
+    V = 20000
+    rng = np.random.default_rng(3)
+    parent = np.array([-1, 0, 0, 1, 2, 3, 3, 5], np.int32)
+    tok = np.array([0, 5, 9, 17000, 4, 12, 13, 8], np.int32)
+    logits = rng.integers(-3, 3, size=(8, V)).astype(np.float32)  # many ties
+    logits[0, 5] = 7.0
+    logits[0, 17] = 7.0           # tie with a later index: 5 wins
+    logits[1, :] = -0.0
+    logits[1, 17000] = 0.0        # -0 == +0: index 0 wins
+    logits[2, :] = np.nan         # all NaN -> 0
+    logits[3, ::3] = np.nan
+    logits[3, 4] = 100.0
+    logits[4, :] = -np.inf
+    logits[4, 12345] = np.nan     # NaN below -inf
+    logits[5, 9999] = np.inf
+    check(logits, parent, tok)
+
+
+def test_duplicate_sibling_tokens():
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        n = int(rng.integers(1, 30))
+        parent = synth.draft_tree(rng, n, 8, p_spine=float(rng.random()))
+        V = int(rng.integers(2, 5))
+        tok = rng.integers(0, V, size=n).astype(np.int32)
+        logits = rng.integers(-1, 2, size=(n, V)).astype(np.float32)
+        check(logits, parent, tok)
+
+
+def test_64_node_tree():
+    rng = np.random.default_rng(64)
+    parent = synth.draft_tree(rng, 64, 16)
+    tok = synth.sibling_distinct_tokens(rng, parent, 1000)
+    logits, L, _ = synth.planted_logits(rng, parent, tok, 1000)
+    assert check(logits, parent, tok)[0] == L

@@ -1,0 +1,210 @@
+"""GPU parity of tree_verify_attn against the CPU oracle.
+
+Bar: row-normalised relative error <= 2e-3 (fp16 products, fp32
+accumulation). Small workloads are compared element by element on every
+row; the 128K and 32K workloads on sampled rows the oracle computes one by
+one. Edge cases cover empty and ragged caches, windows, every tile layout of
+the split kernel, strided caches, extreme Q4_0 scales and peaky scores.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, gpu_attn, rownorm_err
+
+pytestmark = pytest.mark.gpu
+
+
+def deq_copy(inp):
+    """The same tensor stored as F16 (fp16 rounding of the Q4_0 values)."""
+    D = inp["head_dim"]
+    out = dict(inp)
+    out["k_cache"] = oracle.q4_0_dequant(inp["k_cache"], D).astype(np.float16)
+    out["v_cache"] = oracle.q4_0_dequant(inp["v_cache"], D).astype(np.float16)
+    return out
+
+
+def sample_rows(n, Hq, k, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, n * Hq - 1, (n - 1) * Hq, Hq - 1}
+    while len(rows) < k:
+        rows.add(int(rng.integers(n * Hq)))
+    return sorted(rows)
+
+
+def check_rows(got, ref, rows, Hq):
+    g = np.stack([got[r // Hq, r % Hq] for r in rows]).astype(np.float64)
+    f = np.stack([ref[r // Hq, r % Hq] for r in rows])
+    return rownorm_err(g, f)
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16copy"])
+def test_tiny(kv):
+    inp = synth.attn_inputs(**synth.WORKLOADS["tiny"])
+    if kv == "f16copy":
+        inp = deq_copy(inp)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16copy"])
+def test_27b_shape_8k(kv):
+    inp = synth.attn_inputs(**synth.WORKLOADS["27b"])
+    if kv == "f16copy":
+        inp = deq_copy(inp)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_27b_shape_f16_direct():
+    inp = synth.attn_inputs(**synth.WORKLOADS["27b"], kv="f16")
+    rows = sample_rows(23, 24, 48, 5)
+    err = check_rows(gpu_attn(inp), oracle.attn(inp, rows=rows), rows, 24)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("tree", ["budget22", "chain16"])
+def test_long_128k_sampled(tree):
+    w = dict(synth.WORKLOADS["long"])
+    parent = synth.chain_tree(16) if tree == "chain16" else None
+    inp = synth.attn_inputs(**w, parent=parent)
+    n = len(inp["parent"])
+    rows = sample_rows(n, 24, 16, 3)
+    err = check_rows(gpu_attn(inp), oracle.attn(inp, rows=rows), rows, 24)
+    assert err <= TOL, err
+
+
+def test_window_61k():
+    w = dict(synth.WORKLOADS["window"])
+    inp = synth.attn_inputs(**w)
+    got = gpu_attn(inp)
+    err = rownorm_err(got.astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+    # the same as full attention over the last 2048 rows
+    trunc = dict(inp, window=0, k_cache=inp["k_cache"][:, -2048:], v_cache=inp["v_cache"][:, -2048:])
+    assert rownorm_err(gpu_attn(trunc).astype(np.float64), got.astype(np.float64)) <= TOL
+
+
+def test_full_step_layers_sampled():
+    """Two layers (first and last) of the 16-layer, 32K verify step."""
+    w = dict(synth.WORKLOADS["full"])
+    for layer in (0, 15):
+        inp = synth.attn_inputs(**dict(w, seed=5000 + 100 * layer))
+        rows = sample_rows(23, 24, 12, layer)
+        err = check_rows(gpu_attn(inp), oracle.attn(inp, rows=rows), rows, 24)
+        assert err <= TOL, (layer, err)
+
+
+# Head layouts and tree sizes that hit every tile layout of the split kernel:
+# M = (H_q / H_kv) * n query rows per KV head -> T = ceil(M / 16) tiles.
+LAYOUTS = [
+    (2, 1, 1, 64),     # M=2,   T=1
+    (2, 1, 16, 64),    # M=32,  T=2
+    (6, 1, 8, 128),    # M=48,  T=3
+    (4, 1, 16, 64),    # M=64,  T=4
+    (6, 2, 13, 256),   # M=39 per KV head, T=3, two KV heads
+    (5, 1, 16, 128),   # M=80,  T=5
+    (6, 1, 16, 256),   # M=96,  T=6 (chain-16 shape)
+    (7, 1, 16, 64),    # M=112, T=7
+    (8, 1, 16, 128),   # M=128, T=8
+    (6, 1, 23, 256),   # M=138, T=9 (budget-22 shape)
+    (10, 1, 16, 64),   # M=160, T=10 -> two row groups
+    (11, 1, 16, 128),  # M=176, T=11
+    (12, 1, 16, 256),  # M=192, T=12
+    (13, 1, 16, 64),   # M=208, T=13 -> three row groups
+    (6, 1, 64, 256),   # M=384, T=24, 64 nodes
+    (32, 4, 40, 128),  # G=8, 40 nodes
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,n,D", LAYOUTS)
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+def test_tile_layouts(Hq, Hkv, n, D, kv):
+    inp = synth.attn_inputs(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_ctx=700, n_nodes=n,
+                            depth_cap=16, seed=1000 + Hq * 7 + n, kv=kv)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("n_ctx", [0, 1, 5, 63, 64, 65, 127, 255, 1000, 4097])
+def test_ragged_and_empty_caches(n_ctx):
+    w = dict(synth.WORKLOADS["27b"], n_ctx=max(n_ctx, 1))
+    inp = synth.attn_inputs(**w)
+    inp["k_cache"] = inp["k_cache"][:, :n_ctx]
+    inp["v_cache"] = inp["v_cache"][:, :n_ctx]
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("W", [1, 63, 64, 100, 2047, 2048, 5000, 10 ** 9])
+def test_windows(W):
+    w = dict(synth.WORKLOADS["27b"], n_ctx=4500)
+    inp = synth.attn_inputs(**w)
+    inp["window"] = W
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_budget_zero_decode():
+    w = dict(synth.WORKLOADS["27b"])
+    inp = synth.attn_inputs(**w, parent=np.array([-1], np.int32))
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_token_major_strided_cache():
+    """Cache laid out [token][head][row] (ggml-like) instead of head-major."""
+    import torch
+
+    import tree_verify_attention_ddtree_amd as tv
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=1500))
+    t = {}
+    for k in ("k_cache", "v_cache"):
+        tm = np.ascontiguousarray(inp[k].transpose(1, 0, 2))  # [T][H][row]
+        t[k] = torch.from_numpy(tm).cuda()
+    for k in ("q", "k_tree", "v_tree"):
+        t[k] = torch.from_numpy(inp[k]).cuda()
+    row = inp["k_cache"].shape[2]
+    got = gpu_attn(inp, tensors=t, strides=(row * inp["n_kv_heads"], row))
+    err = rownorm_err(got.astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_extreme_q4_0_scales():
+    """Subnormal, zero and large fp16 scales decode exactly (no flushing)."""
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=900))
+    rng = np.random.default_rng(77)
+    for k in ("k_cache", "v_cache"):
+        c = inp[k].copy()
+        blocks = c.reshape(c.shape[0], c.shape[1], -1, 18)
+        sel = rng.random(blocks.shape[:3])
+        sc = blocks[..., 0:2].copy().view(np.uint16)[..., 0]
+        sc[sel < 0.2] = 0x0001          # smallest subnormal
+        sc[(sel >= 0.2) & (sel < 0.3)] = 0x03FF  # largest subnormal
+        sc[(sel >= 0.3) & (sel < 0.35)] = 0x0000
+        sc[(sel >= 0.35) & (sel < 0.4)] = 0x8000
+        blocks[..., 0:2] = sc[..., None].view(np.uint8).reshape(sc.shape + (2,))
+        inp[k] = c
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_peaky_scores_force_rescaling():
+    """Large, growing scores move the running max by far more than the
+    lazy-rescale threshold many times within a split."""
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=6000), kv="f16")
+    q = inp["q"].astype(np.float32) * 4
+    inp["q"] = q.astype(np.float16)
+    kc = inp["k_cache"].astype(np.float32)
+    ramp = np.linspace(0.2, 6.0, kc.shape[1], dtype=np.float32)[None, :, None]
+    inp["k_cache"] = (kc * ramp).astype(np.float16)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_deterministic():
+    inp = synth.attn_inputs(**synth.WORKLOADS["27b"])
+    a, b = gpu_attn(inp, repeat=2)
+    assert np.array_equal(a, b)

@@ -1,0 +1,125 @@
+"""Host-side checks of libtv.so that need no GPU.
+
+The library must load, export every function include/tree_verify.h
+declares, and reject invalid arguments on the host with the documented
+status codes before it touches the device (these calls make no HIP call).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tree_verify_attention_ddtree_amd as tv
+from tree_verify_attention_ddtree_amd import build as tvbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    tvbuild.ensure_built()
+    return tv.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tree_verify.h")).read()
+    return sorted(set(re.findall(r"^TV_API\s+[\w\s\*]*?\b(\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(tv.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert tv.tv_strerror(code)
+    assert tv.tv_strerror(12345) == "unknown status"
+
+
+def _desc(parent=(-1, 0, 1), Hq=4, Hkv=2, D=64, kv=tv.TV_KV_Q4_0, n_ctx=256, window=0, scale=0.125,
+          ts=36, hs=36 * 256):
+    return tv.make_desc(parent, Hq, Hkv, D, kv, n_ctx, window, scale, ts, hs)
+
+
+def _call(L, desc, ptrs=None, ws=None, wsb=0):
+    if ptrs is None:
+        ptrs = tv.TvAttnPtrs(4096, 4096, 4096, 4096, 4096, 4096)
+    return L.tree_verify_attn(ctypes.byref(desc), ctypes.byref(ptrs), ws, wsb, None)
+
+
+@pytest.mark.parametrize("parent,code", [
+    ((0, 0), -2),          # root must have parent -1
+    ((-1, 1), -2),         # parent must precede child
+    ((-1, 0, 3, 1), -2),   # forward reference
+    ((-1, -1), -2),        # second root
+    (tuple([-1] + list(range(64))), -3),  # 65 nodes
+])
+def test_bad_trees_rejected(L, parent, code):
+    d, keep = _desc(parent=parent)
+    assert _call(L, d) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), -3),       # H_q not a multiple of H_kv
+    (dict(D=96), -3),              # head_dim not supported
+    (dict(kv=7), -1),              # bad KV type
+    (dict(n_ctx=-1), -3),
+    (dict(window=-5), -3),
+    (dict(scale=0.0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(scale=-0.1), -1),
+    (dict(ts=35), -3),             # token stride below the row size
+    (dict(ts=38), -4),             # Q4_0 strides must be multiples of 4
+    (dict(kv=tv.TV_KV_F16, ts=136, hs=136 * 256), -4),  # F16 strides: multiples of 16
+])
+def test_bad_shapes_rejected(L, kw, code):
+    d, keep = _desc(**kw)
+    assert _call(L, d) == code
+
+
+def test_null_and_misaligned_pointers_rejected(L):
+    d, keep = _desc()
+    assert _call(L, d, tv.TvAttnPtrs(4096, 4096, None, 4096, 4096, 4096)) == -1
+    assert _call(L, d, tv.TvAttnPtrs(None, 4096, 4096, 4096, 4096, 4096)) == -1
+    assert _call(L, d, tv.TvAttnPtrs(4096, 4096, 4098, 4096, 4096, 4096)) == -4
+    assert _call(L, d, tv.TvAttnPtrs(4104, 4096, 4096, 4096, 4096, 4096)) == -4
+    # an empty cache may be NULL; the call then fails only later, on the device
+    d0, keep0 = _desc(n_ctx=0)
+    assert _call(L, d0, tv.TvAttnPtrs(None, None, 4096, 4096, 4096, 4096)) not in (-1, -4)
+    assert L.tree_verify_attn(None, None, None, 0, None) == -1
+
+
+def test_accept_argument_checks(L):
+    par = np.array([-1, 0, 0], np.int32)
+    tok = np.array([0, 1, 2], np.int32)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    f = L.tree_accept
+    assert f(4096, 3, 10, P(np.array([0, 0, 0], np.int32)), P(tok), 4096, 4096, 4096, 1 << 20, None) == -2
+    assert f(4096, 3, 0, P(par), P(tok), 4096, 4096, 4096, 1 << 20, None) == -3
+    assert f(4096, 65, 10, P(np.arange(-1, 64, dtype=np.int32)), P(np.zeros(65, np.int32)), 4096, 4096, 4096,
+             1 << 20, None) == -3
+    assert f(None, 3, 10, P(par), P(tok), 4096, 4096, 4096, 1 << 20, None) == -1
+    assert f(4096, 3, 10, P(par), None, 4096, 4096, 4096, 1 << 20, None) == -1
+    assert f(4100, 3, 10, P(par), P(tok), 4096, 4096, 4096, 1 << 20, None) == -4
+    assert f(4096, 3, 10, P(par), P(tok), 4096, 4096, None, 0, None) == -5
+    assert f(4096, 3, 10, P(par), P(tok), 4096, 4096, 4096, 7, None) == -5
+    assert tv.tv_accept_workspace_bytes(23, 152000) == 23 * 19 * 8
+    assert tv.tv_accept_workspace_bytes(0, 10) == 0
+    assert tv.tv_accept_workspace_bytes(3, 0) == 0
+
+
+def test_library_links_no_oracle():
+    """The GPU library and the oracle share nothing: no oracle symbol, no
+    oracle header."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", tvbuild.LIB], capture_output=True, text=True).stdout
+    assert "tvref" not in out
+    for src in os.listdir(tvbuild.CSRC):
+        text = open(os.path.join(tvbuild.CSRC, src)).read()
+        assert "tvref" not in text and "oracle" not in text.lower(), src

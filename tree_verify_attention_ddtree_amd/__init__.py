@@ -1,0 +1,171 @@
+"""Python binding of libtv.so: DDTree tree-verify attention and greedy
+acceptance on MI355X (gfx950).
+
+The functions carry the names of the C ABI in include/tree_verify.h and only
+marshal arguments: torch tensors become device pointers, host arrays become
+int32 buffers, and a non-zero status becomes an exception. Every step of the
+computation runs in the HIP kernels of libtv.so; there is no fallback. The
+library must have been built (``python -m tree_verify_attention_ddtree_amd.build``
+or ``__graft_entry__.build()``); importing works without it, calling does not.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+TV_OK = 0
+TV_KV_F16 = 0
+TV_KV_Q4_0 = 1
+TV_MAX_NODES = 64
+
+_lib = None
+
+
+class TvAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_nodes", ctypes.c_int32),
+        ("parent", ctypes.c_void_p),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_type", ctypes.c_int32),
+        ("n_ctx", ctypes.c_int64),
+        ("window", ctypes.c_int64),
+        ("kv_token_stride", ctypes.c_int64),
+        ("kv_head_stride", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class TvAttnPtrs(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("k_tree", ctypes.c_void_p),
+        ("v_tree", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
+class TvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {tv_strerror(code)} ({code})")
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """The loaded libtv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is missing: build it first (python -m tree_verify_attention_ddtree_amd.build)")
+        L = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        L.tv_strerror.argtypes = [ctypes.c_int]
+        L.tv_strerror.restype = ctypes.c_char_p
+        L.tv_attn_workspace_bytes.argtypes = [ctypes.POINTER(TvAttnDesc)]
+        L.tv_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.tree_verify_attn.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.POINTER(TvAttnPtrs), P, ctypes.c_size_t, P]
+        L.tree_verify_attn.restype = ctypes.c_int
+        L.tv_accept_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.tv_accept_workspace_bytes.restype = ctypes.c_size_t
+        L.tree_accept.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, ctypes.c_size_t, P]
+        L.tree_accept.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("tree_verify_attn", "tree_accept", "tv_attn_workspace_bytes", "tv_accept_workspace_bytes",
+           "tv_strerror")
+
+
+def tv_strerror(code: int) -> str:
+    return lib().tv_strerror(int(code)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(int(t.data_ptr()))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def make_desc(parent, n_q_heads, n_kv_heads, head_dim, kv_type, n_ctx, window, scale, kv_token_stride=0,
+              kv_head_stride=0):
+    """A TvAttnDesc plus the int32 buffer its parent pointer refers to (keep
+    both alive while the descriptor is used)."""
+    par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
+    d = TvAttnDesc(len(par), par.ctypes.data_as(ctypes.c_void_p).value, int(n_q_heads), int(n_kv_heads),
+                   int(head_dim), int(kv_type), int(n_ctx), int(window), int(kv_token_stride),
+                   int(kv_head_stride), float(scale))
+    return d, par
+
+
+def cache_strides(cache, kv_type):
+    """Token and head strides in bytes of a head-major cache tensor
+    [H_kv, T, row] (uint8 rows for Q4_0, fp16 rows for F16)."""
+    es = cache.element_size()
+    return cache.stride(1) * es, cache.stride(0) * es
+
+
+def tv_attn_workspace_bytes(desc: TvAttnDesc) -> int:
+    return int(lib().tv_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def tree_verify_attn(desc: TvAttnDesc, k_cache, v_cache, q, k_tree, v_tree, out, workspace=None,
+                     workspace_bytes=None, stream=None) -> None:
+    """One layer of tree-verify attention (see include/tree_verify.h).
+
+    Tensors are device tensors: caches laid out as the descriptor's strides
+    say, q / k_tree / v_tree fp16, out fp32. ``workspace`` is a device
+    tensor of at least tv_attn_workspace_bytes(desc) bytes (or None when that
+    is 0).
+    """
+    ptrs = TvAttnPtrs(*(p.value if p is not None else None for p in
+                        (_ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out))))
+    wsb = workspace_bytes
+    if wsb is None:
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().tree_verify_attn(ctypes.byref(desc), ctypes.byref(ptrs), _ptr(workspace), int(wsb),
+                                _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_verify_attn")
+
+
+def tv_accept_workspace_bytes(n_nodes: int, vocab: int) -> int:
+    return int(lib().tv_accept_workspace_bytes(int(n_nodes), int(vocab)))
+
+
+def tree_accept(logits, parent, tokens, argmax_out, result_out, workspace, stream=None) -> None:
+    """Greedy acceptance (see include/tree_verify.h). ``logits`` is a device
+    fp32 [n, vocab] tensor, ``parent``/``tokens`` host int sequences,
+    ``argmax_out`` device int32 [n], ``result_out`` device int32 [2 + 2n]."""
+    n, vocab = int(logits.shape[0]), int(logits.shape[1])
+    par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
+    tok = np.ascontiguousarray(np.asarray(tokens), dtype=np.int32)
+    if len(par) != n or len(tok) != n:
+        raise ValueError("parent/tokens length must equal logits.shape[0]")
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().tree_accept(_ptr(logits), n, vocab, par.ctypes.data_as(ctypes.c_void_p),
+                           tok.ctypes.data_as(ctypes.c_void_p), _ptr(argmax_out), _ptr(result_out),
+                           _ptr(workspace), int(wsb), _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_accept")

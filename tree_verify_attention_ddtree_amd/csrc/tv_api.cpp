@@ -1,0 +1,203 @@
+// C ABI of libtv.so: argument checks, planning, workspace sizes, launches.
+// Every check runs on the host before anything is launched.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
+                hipStream_t stream);
+size_t accept_ws_bytes(int n, int vocab);
+int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
+                  int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
+
+// Splits are sized so one launch fills the device with about one workgroup
+// per compute unit, but never below kMinChunks chunks (256 keys) per split:
+// a split's fixed cost (Q fragments, writing its partial state) has to be
+// amortised over its keys.
+constexpr int kMinChunks = 4;
+
+static int check_tree(int n, const int32_t *parent)
+{
+    if (n < 1 || n > TV_MAX_NODES) return TV_E_SHAPE;
+    if (!parent) return TV_E_ARG;
+    if (parent[0] != -1) return TV_E_TREE;
+    for (int i = 1; i < n; ++i)
+        if (parent[i] < 0 || parent[i] >= i) return TV_E_TREE;
+    return TV_OK;
+}
+
+static int check_desc(const tv_attn_desc *d)
+{
+    if (!d) return TV_E_ARG;
+    int rc = check_tree(d->n_nodes, d->parent);
+    if (rc) return rc;
+    if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads) return TV_E_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return TV_E_SHAPE;
+    if (d->kv_type != TV_KV_F16 && d->kv_type != TV_KV_Q4_0) return TV_E_ARG;
+    if (d->n_ctx < 0 || d->window < 0) return TV_E_SHAPE;
+    if (!(d->scale > 0.0f) || !isfinite(d->scale)) return TV_E_ARG;
+    if ((int64_t)d->n_nodes * d->n_q_heads > (int64_t)1 << 24) return TV_E_SHAPE;
+    if (d->n_ctx > 0) {
+        const int64_t row = d->kv_type == TV_KV_Q4_0 ? (int64_t)d->head_dim / 32 * 18 : (int64_t)d->head_dim * 2;
+        const int64_t al = d->kv_type == TV_KV_Q4_0 ? 4 : 16;
+        if (d->kv_token_stride < row || d->kv_head_stride < 0) return TV_E_SHAPE;
+        if (d->kv_token_stride % al || d->kv_head_stride % al) return TV_E_ALIGN;
+    }
+    return TV_OK;
+}
+
+static int plan_rows(int M, RowPlan *rp)
+{
+    const int T = (M + 15) / 16;
+    for (int RG = 1; RG <= T; ++RG) {
+        int nown = 0, nsh = 0;
+        for (int g = 0; g < RG; ++g) {
+            const int Tg = T / RG + (g < T % RG ? 1 : 0);
+            int o, s;
+            group_roles(Tg, &o, &s);
+            nown = o > nown ? o : nown;
+            nsh = s > nsh ? s : nsh;
+        }
+        if (nown + nsh <= kMaxSlots && nown + nsh >= 1) {
+            rp->tiles = T;
+            rp->groups = RG;
+            rp->nown = nown;
+            rp->nsh = nsh;
+            return TV_OK;
+        }
+    }
+    return TV_E_SHAPE;
+}
+
+int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
+{
+    const int G = d->n_q_heads / d->n_kv_heads;
+    const int M = G * d->n_nodes;
+    int rc = plan_rows(M, &out->rows);
+    if (rc) return rc;
+    out->s0 = (d->window > 0 && d->n_ctx > d->window) ? d->n_ctx - d->window : 0;
+    out->R = d->n_ctx - out->s0;
+    out->n_chunks = (out->R + kChunk - 1) / kChunk;
+    if (out->n_chunks == 0) {
+        out->S = 0;
+        return TV_OK;
+    }
+    const int64_t per = (int64_t)d->n_kv_heads * out->rows.groups;
+    int64_t S = (n_cu + per - 1) / per;
+    int64_t cap = out->n_chunks / kMinChunks;
+    if (cap < 1) cap = 1;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    if (S > 65535) S = 65535;
+    out->S = (int)S;
+    return TV_OK;
+}
+
+size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p)
+{
+    const size_t NR = (size_t)d->n_nodes * d->n_q_heads;
+    return (size_t)p.S * NR * ((size_t)d->head_dim + 2) * sizeof(float);
+}
+
+int device_cu_count(int *n_cu)
+{
+    // cached per device; the count of a device never changes
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TV_E_HIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *n_cu = c;
+            return TV_OK;
+        }
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+        return TV_E_HIP;
+    if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    *n_cu = v;
+    return TV_OK;
+}
+
+}  // namespace tv
+
+extern "C" {
+
+const char *tv_strerror(int code)
+{
+    switch (code) {
+    case TV_OK: return "ok";
+    case TV_E_ARG: return "invalid argument";
+    case TV_E_TREE: return "parent array is not a rooted tree in topological order";
+    case TV_E_SHAPE: return "unsupported shape";
+    case TV_E_ALIGN: return "misaligned pointer or stride";
+    case TV_E_WORKSPACE: return "workspace missing or too small";
+    case TV_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t tv_attn_workspace_bytes(const tv_attn_desc *d)
+{
+    if (tv::check_desc(d)) return 0;
+    int n_cu = 0;
+    if (tv::device_cu_count(&n_cu)) return 0;
+    tv::SplitPlan plan;
+    if (tv::plan_attn(d, n_cu, &plan)) return 0;
+    return tv::attn_ws_bytes(d, plan);
+}
+
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    int rc = tv::check_desc(d);
+    if (rc) return rc;
+    if (!p || !p->q || !p->k_tree || !p->v_tree || !p->out) return TV_E_ARG;
+    if (d->n_ctx > 0 && (!p->k_cache || !p->v_cache)) return TV_E_ARG;
+    if (!aligned(p->q, 16) || !aligned(p->k_tree, 16) || !aligned(p->v_tree, 16) || !aligned(p->out, 16))
+        return TV_E_ALIGN;
+    if (d->n_ctx > 0 && (!aligned(p->k_cache, 16) || !aligned(p->v_cache, 16))) return TV_E_ALIGN;
+    int n_cu = 0;
+    rc = tv::device_cu_count(&n_cu);
+    if (rc) return rc;
+    tv::SplitPlan plan;
+    rc = tv::plan_attn(d, n_cu, &plan);
+    if (rc) return rc;
+    const size_t need = tv::attn_ws_bytes(d, plan);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return TV_E_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return TV_E_ALIGN;
+    return tv::launch_attn(d, p, plan, workspace, (hipStream_t)stream);
+}
+
+size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab)
+{
+    if (n_nodes < 1 || n_nodes > TV_MAX_NODES || vocab < 1) return 0;
+    return tv::accept_ws_bytes(n_nodes, vocab);
+}
+
+int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent, const int32_t *tokens,
+                int32_t *argmax_out, int32_t *result_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = tv::check_tree(n_nodes, parent);
+    if (rc) return rc;
+    if (vocab < 1) return TV_E_SHAPE;
+    if (!logits || !tokens || !argmax_out || !result_out) return TV_E_ARG;
+    if (!aligned(logits, 16) || !aligned(argmax_out, 4) || !aligned(result_out, 4)) return TV_E_ALIGN;
+    const size_t need = tv::accept_ws_bytes(n_nodes, vocab);
+    if (!workspace || workspace_bytes < need) return TV_E_WORKSPACE;
+    if (!aligned(workspace, 8)) return TV_E_ALIGN;
+    return tv::launch_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out, workspace,
+                             (hipStream_t)stream);
+}
+
+}  // extern "C"

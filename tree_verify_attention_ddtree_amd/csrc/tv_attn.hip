@@ -1,0 +1,800 @@
+// Tree-verify attention for gfx950: split-K flash decode over the committed
+// KV cache with the whole packed (GQA group x tree node) query block of one KV
+// head held by one workgroup, then a merge kernel that adds each node's tree
+// ancestors and combines the splits.
+//
+// Method: the target model scores all nodes of a DDTree draft tree in one
+// verify pass; each node attends to the committed KV cache (F16 or Q4_0,
+// optionally limited to a 2048-token sliding window at decode) and, inside
+// the tree, to its ancestors. Sources: "Luce DFlash: 単一RTX 3090で最大2倍の
+// スループットを目指すQwen3.6-27B", feature list (DDTree tree verify with
+// budget 22 and block size 16, greedy verify, Q4_0 KV up to about 128K,
+// sliding-window flash attention with a 2048-token window); "We got 207 tok/s
+// with Qwen3.5-27B on an RTX 3090", "What we built vs what we didn't" (DDTree
+// tree-structured verify; Q4_0 KV cache to fit 128K).
+//
+// Split kernel, one workgroup = 4 wave64s per (key-range split, KV head, row
+// group):
+//   * Rows: the M = G * n query rows of a KV head (row r = node r/G, query
+//     head g*G + r%G) are cut into 16-row tiles. Each wave owns whole tiles;
+//     one or two left-over tiles are "shared": every wave computes them over
+//     its own quarter (16 keys) of each 64-key chunk and the four partial
+//     softmax states are merged through LDS at the end.
+//   * Keys stream in 64-row chunks, double-buffered in LDS. Every thread
+//     loads raw Q4_0 bytes (or fp16) for the next chunk into registers while
+//     the current chunk is computed, then dequantises in registers (fp16 bit
+//     tricks, exact code - 8, one rounding when the fp16 scale is applied)
+//     and writes K row-major and V transposed into LDS.
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_f16 with fp32
+//     accumulation; Q fragments stay in registers, the O accumulators too.
+//   * Online softmax in the exp2 domain with a lazy rescale (the running max
+//     only moves when a chunk's max exceeds it by more than 2^8), P rounded to
+//     fp16 and its row sums taken from the rounded values.
+
+#include <math.h>
+#include <string.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32;
+
+// Keeps the scheduler from hoisting every LDS fragment load of an unrolled
+// loop to its top, which would need a register per fragment.
+#ifndef TV_NO_FENCE
+#define TV_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define TV_SCHED_FENCE()
+#endif
+
+constexpr float kTau = 8.0f;
+constexpr float kNegBig = -1.0e30f;
+
+struct SplitArgs {
+    const uint8_t *k_cache;
+    const uint8_t *v_cache;
+    int64_t tok_stride;
+    int64_t head_stride;
+    const _Float16 *q;
+    float *ws_o;   // [S][NR][D] unnormalised partial outputs
+    float *ws_ml;  // [S][NR][2] running max (log2 units) and row sum
+    int64_t s0;
+    int64_t key_end;
+    int64_t n_chunks;
+    int32_t NR;  // n * H_q
+    int32_t H_q;
+    int32_t G;
+    int32_t M;  // G * n
+    int32_t S;
+    float c;  // scale * log2(e)
+};
+
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2 as_h2(u32 x) { return __builtin_bit_cast(h2, x); }
+
+// fp32 pair -> fp16 pair (round toward zero), one instruction
+__device__ __forceinline__ h2 pk_rtz(float a, float b)
+{
+    return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// acc + p.x + p.y in fp32 (exact products with 1, fp32 sums)
+__device__ __forceinline__ float add_pair(h2 p, float acc)
+{
+    const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, p), one, acc, false);
+}
+
+// 8 Q4_0 codes packed in one dword (code bytes 4k..4k+3 of a block) -> the
+// exact values code - 8 as four fp16 pairs: [0] = elements (4k, 4k+2),
+// [1] = (4k+1, 4k+3), [2] = (4k+16, 4k+18), [3] = (4k+17, 4k+19).
+// 0x6400 | c is fp16 1024 + c; 0x6400 | (c << 4) is 1024 + 16 c.
+__device__ __forceinline__ void q4_unpack(u32 x, h2 v[4])
+{
+    const u32 y = x >> 8;
+    const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    v[0] = as_h2((x & 0x000F000Fu) | 0x64006400u) - off;
+    v[1] = as_h2((y & 0x000F000Fu) | 0x64006400u) - off;
+    v[2] = __builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+    v[3] = __builtin_elementwise_fma(as_h2((y & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+}
+
+// Position of chunk key kappa (0..63) in a transposed V row: inside each group
+// of 32 keys, the 8 keys a lane group of the PV MFMA consumes are contiguous.
+__device__ __forceinline__ int vpos(int kappa)
+{
+    return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
+}
+
+template <int D, int KVT>
+struct Stage {
+    static constexpr int NB = D / 32;   // 32-wide blocks per row
+    static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
+    static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
+    static constexpr int VSTR = kChunk + 8;  // V^T row stride in LDS (halves)
+    static constexpr int KELEMS = kChunk * KSTR;
+    static constexpr int VELEMS = D * VSTR;
+    static constexpr int ELEMS = KELEMS + VELEMS;
+    // raw registers per thread for the next chunk
+    static constexpr int RAW = KVT == TV_KV_Q4_0 ? NK * 5 : NK * 16;
+};
+
+// Thread t of the 256 handles K (t < 128) or V (t >= 128), NK consecutive
+// keys of the chunk and one 32-value block of those rows.
+template <int D, int KVT>
+__device__ __forceinline__ void load_raw(const SplitArgs &a, int gkv, int64_t kbase, int tid, u32 *raw)
+{
+    using St = Stage<D, KVT>;
+    const int isv = tid >> 7, u = tid & 127;
+    const int b = u % St::NB, key0 = (u / St::NB) * St::NK;
+    const uint8_t *base = (isv ? a.v_cache : a.k_cache) + (int64_t)gkv * a.head_stride;
+#pragma unroll
+    for (int kk = 0; kk < St::NK; ++kk) {
+        const int64_t row = kbase + key0 + kk;
+        if constexpr (KVT == TV_KV_Q4_0) {
+            if (row < a.key_end) {
+                const u32 *p = (const u32 *)(base + row * a.tok_stride + ((18 * b) & ~3));
+#pragma unroll
+                for (int j = 0; j < 5; ++j) raw[kk * 5 + j] = p[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 5; ++j) raw[kk * 5 + j] = 0u;
+            }
+        } else {
+            if (row < a.key_end) {
+                const uint4 *p = (const uint4 *)(base + row * a.tok_stride + 64 * b);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 t = p[j];
+                    raw[kk * 16 + 4 * j + 0] = t.x;
+                    raw[kk * 16 + 4 * j + 1] = t.y;
+                    raw[kk * 16 + 4 * j + 2] = t.z;
+                    raw[kk * 16 + 4 * j + 3] = t.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) raw[kk * 16 + j] = 0u;
+            }
+        }
+    }
+}
+
+// Dequantise the raw registers and write them into one LDS stage:
+//   K:   ks[key][32b + 8k + j], for Q4_0 the 8 values of code dword k in the
+//        order of q4_unpack; for F16 the natural order.
+//   V^T: vt[d][vpos(key)].
+template <int D, int KVT>
+__device__ __forceinline__ void store_stage(const u32 *raw, _Float16 *ks, _Float16 *vt, int tid)
+{
+    using St = Stage<D, KVT>;
+    const int isv = tid >> 7, u = tid & 127;
+    const int b = u % St::NB, key0 = (u / St::NB) * St::NK;
+    if constexpr (KVT == TV_KV_Q4_0) {
+        // code dwords and scale of key kk: block starts at byte 18b of the row;
+        // the 5 raw dwords start at (18b & ~3).
+        u32 cw[St::NK][4];
+        _Float16 sc[St::NK];
+#pragma unroll
+        for (int kk = 0; kk < St::NK; ++kk) {
+            const u32 *r = raw + kk * 5;
+            if (b & 1) {  // block at 2 mod 4: scale in the high half of r[0]
+                sc[kk] = __builtin_bit_cast(_Float16, (uint16_t)(r[0] >> 16));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cw[kk][k] = r[k + 1];
+            } else {  // block at 0 mod 4: codes start 2 bytes into r[0]
+                sc[kk] = __builtin_bit_cast(_Float16, (uint16_t)(r[0] & 0xFFFFu));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cw[kk][k] = (r[k] >> 16) | (r[k + 1] << 16);
+            }
+        }
+        if (!isv) {
+#pragma unroll
+            for (int kk = 0; kk < St::NK; ++kk) {
+                const h2 s2 = {sc[kk], sc[kk]};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    h2 v[4];
+                    q4_unpack(cw[kk][k], v);
+                    h8 o;
+                    o.s01 = v[0] * s2;
+                    o.s23 = v[1] * s2;
+                    o.s45 = v[2] * s2;
+                    o.s67 = v[3] * s2;
+                    *(h8 *)(ks + (key0 + kk) * St::KSTR + 32 * b + 8 * k) = o;
+                }
+            }
+        } else {
+            const int p0 = vpos(key0);
+            if constexpr (St::NK >= 2) {
+                // pairs of keys: interleave their code bytes so every fp16
+                // pair holds one element of two keys
+#pragma unroll
+                for (int pr = 0; pr < St::NK / 2; ++pr) {
+                    const h2 s2 = {sc[2 * pr], sc[2 * pr + 1]};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const u32 x0 = cw[2 * pr][k], x1 = cw[2 * pr + 1][k];
+                        const u32 za = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+                        const u32 zb = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+                        h2 va[4], vb[4];
+                        q4_unpack(za, va);  // elements 4k, 4k+1, 4k+16, 4k+17
+                        q4_unpack(zb, vb);  // elements 4k+2, 4k+3, 4k+18, 4k+19
+                        const int e[8] = {4 * k, 4 * k + 1, 4 * k + 16, 4 * k + 17,
+                                          4 * k + 2, 4 * k + 3, 4 * k + 18, 4 * k + 19};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            *(h2 *)(vt + (32 * b + e[t]) * St::VSTR + p0 + 2 * pr) = va[t] * s2;
+                            *(h2 *)(vt + (32 * b + e[4 + t]) * St::VSTR + p0 + 2 * pr) = vb[t] * s2;
+                        }
+                    }
+                }
+            } else {
+                const h2 s2 = {sc[0], sc[0]};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    h2 v[4];
+                    q4_unpack(cw[0][k], v);
+                    const int e[8] = {4 * k, 4 * k + 2, 4 * k + 1, 4 * k + 3,
+                                      4 * k + 16, 4 * k + 18, 4 * k + 17, 4 * k + 19};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const h2 w = v[t] * s2;
+                        vt[(32 * b + e[2 * t]) * St::VSTR + p0] = w.x;
+                        vt[(32 * b + e[2 * t + 1]) * St::VSTR + p0] = w.y;
+                    }
+                }
+            }
+        }
+    } else {
+        if (!isv) {
+#pragma unroll
+            for (int kk = 0; kk < St::NK; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint4 t;
+                    t.x = raw[kk * 16 + 4 * j];
+                    t.y = raw[kk * 16 + 4 * j + 1];
+                    t.z = raw[kk * 16 + 4 * j + 2];
+                    t.w = raw[kk * 16 + 4 * j + 3];
+                    *(uint4 *)(ks + (key0 + kk) * St::KSTR + 32 * b + 8 * j) = t;
+                }
+        } else {
+            const int p0 = vpos(key0);
+            if constexpr (St::NK >= 2) {
+#pragma unroll
+                for (int pr = 0; pr < St::NK / 2; ++pr)
+#pragma unroll
+                    for (int w = 0; w < 16; ++w) {
+                        const u32 x0 = raw[(2 * pr) * 16 + w], x1 = raw[(2 * pr + 1) * 16 + w];
+                        // dword w holds elements 2w, 2w+1 of the block
+                        *(u32 *)(vt + (32 * b + 2 * w) * St::VSTR + p0 + 2 * pr) =
+                            __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+                        *(u32 *)(vt + (32 * b + 2 * w + 1) * St::VSTR + p0 + 2 * pr) =
+                            __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+                    }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 16; ++w) {
+                    const h2 v = as_h2(raw[w]);
+                    vt[(32 * b + 2 * w) * St::VSTR + p0] = v.x;
+                    vt[(32 * b + 2 * w + 1) * St::VSTR + p0] = v.y;
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float wave_max_16_32(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum_16_32(float x)
+{
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Rescale one query tile's state when its chunk max mnew exceeds the running
+// max by more than kTau anywhere in the wave.
+template <int NDT>
+__device__ __forceinline__ void maybe_rescale(float mnew, float &m, float &l, f4 (&o)[NDT])
+{
+    const bool need = mnew > m + kTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mm = fmaxf(m, mnew);
+        const float f = __builtin_amdgcn_exp2f(m - mm);
+        l *= f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
+        m = mm;
+    }
+}
+
+template <int D, int KVT, int NOWN, int NSH>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+split_kernel(const SplitArgs a)
+{
+    using St = Stage<D, KVT>;
+    constexpr int NB = St::NB;
+    constexpr int NDT = D / 16;
+    constexpr int NS = NOWN + NSH;
+    static_assert(NS >= 1 && NS <= kMaxSlots, "slots");
+    __shared__ __attribute__((aligned(16))) _Float16 lds[2 * St::ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x, gkv = blockIdx.y, rg = blockIdx.z;
+
+    // ---- tiles of this row group: own tile k of wave w is t0 + 4k + w, shared
+    // tile u is t0 + 4*NOWN + u; tiles at or past t0 + Tg are padding (zero
+    // queries, results dropped), so every wave runs the same instructions.
+    const int T = (a.M + 15) / 16;
+    const int RG = gridDim.z;
+    const int tb = T / RG, te = T % RG;
+    const int Tg = tb + (rg < te ? 1 : 0);
+    const int t0 = rg * tb + (rg < te ? rg : te);
+    const int t_end = t0 + Tg;
+    int tile[NS];
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) tile[k] = t0 + 4 * k + w;
+#pragma unroll
+    for (int u = 0; u < NSH; ++u) tile[NOWN + u] = t0 + 4 * NOWN + u;
+
+    // ---- Q fragments (B operand of S^T = K Q^T), zero for padding rows
+    h8 qf[NS][NB];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int r = 16 * tile[k] + col;
+        if (tile[k] < t_end && r < a.M) {
+            const int node = r / a.G, h = gkv * a.G + r % a.G;
+            const _Float16 *qr = a.q + ((int64_t)node * a.H_q + h) * D;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                if constexpr (KVT == TV_KV_Q4_0) {
+                    const h4 lo = *(const h4 *)(qr + 32 * bb + 4 * grp);
+                    const h4 hi = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
+                    h8 f;
+                    f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
+                    f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
+                    qf[k][bb] = f;
+                } else {
+                    qf[k][bb] = *(const h8 *)(qr + 32 * bb + 8 * grp);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) qf[k][bb] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+
+    // The Q fragments are read only as MFMA B operands, which may come from
+    // AGPRs; parking them there leaves the VGPRs to the accumulators.
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) asm volatile("" : "+a"(qf[k][bb]));
+
+    f4 o[NS][NDT];
+    float m[NS], l[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        m[k] = kNegBig;
+        l[k] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[k][dt] = (f4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int64_t c_begin = a.n_chunks * split / a.S;
+    const int64_t c_end = a.n_chunks * (split + 1) / a.S;
+
+    u32 raw[St::RAW];
+    if (c_begin < c_end) load_raw<D, KVT>(a, gkv, a.s0 + c_begin * kChunk, tid, raw);
+
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int st = (int)((c - c_begin) & 1);
+        _Float16 *ks = lds + st * St::ELEMS;
+        _Float16 *vt = ks + St::KELEMS;
+        store_stage<D, KVT>(raw, ks, vt, tid);
+        if (c + 1 < c_end) load_raw<D, KVT>(a, gkv, a.s0 + (c + 1) * kChunk, tid, raw);
+        __syncthreads();
+
+        const int64_t kbase = a.s0 + c * kChunk;
+        const bool ragged = kbase + kChunk > a.key_end;
+
+        // ---- S^T tiles: 4 key tiles x own slots, key tile w x shared slots
+        f4 sacc[NOWN > 0 ? NOWN : 1][4];
+        f4 ssh[NSH > 0 ? NSH : 1];
+#pragma unroll
+        for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sacc[k][kt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            if constexpr (NOWN > 0) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const h8 kf = *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
+#pragma unroll
+                    for (int k = 0; k < NOWN; ++k)
+                        sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[k][bb], sacc[k][kt], 0, 0, 0);
+                }
+            }
+            if constexpr (NSH > 0) {
+                const h8 kf = *(const h8 *)(ks + (16 * w + col) * St::KSTR + 32 * bb + 8 * grp);
+#pragma unroll
+                for (int u = 0; u < NSH; ++u)
+                    ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[NOWN + u][bb], ssh[u], 0, 0, 0);
+            }
+            TV_SCHED_FENCE();
+        }
+
+        // ---- online softmax -> fp16 P^T fragments
+        h8 pf[NOWN > 0 ? NOWN : 1][2];
+        h8 psh[NSH > 0 ? NSH : 1];
+#pragma unroll
+        for (int k = 0; k < NOWN; ++k) {
+            {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = sacc[k][kt][i];
+                        if (ragged && kbase + 16 * kt + 4 * grp + i >= a.key_end) v = -INFINITY;
+                        sacc[k][kt][i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                mx = wave_max_16_32(mx);
+                maybe_rescale<NDT>(mx * a.c, m[k], l[k], o[k]);
+                float p[4][4];
+                float ls = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k][kt][i], a.c, -m[k]));
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const h2 p0 = pk_rtz(p[2 * kk][0], p[2 * kk][1]);
+                    const h2 p1 = pk_rtz(p[2 * kk][2], p[2 * kk][3]);
+                    const h2 p2 = pk_rtz(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+                    const h2 p3 = pk_rtz(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+                    ls = add_pair(p0, ls);
+                    ls = add_pair(p1, ls);
+                    ls = add_pair(p2, ls);
+                    ls = add_pair(p3, ls);
+                    h8 f;
+                    f.s01 = p0;
+                    f.s23 = p1;
+                    f.s45 = p2;
+                    f.s67 = p3;
+                    pf[k][kk] = f;
+                }
+                l[k] += ls;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NSH; ++u) {
+            {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = ssh[u][i];
+                    if (ragged && kbase + 16 * w + 4 * grp + i >= a.key_end) v = -INFINITY;
+                    ssh[u][i] = v;
+                    mx = fmaxf(mx, v);
+                }
+                mx = wave_max_16_32(mx);
+                maybe_rescale<NDT>(mx * a.c, m[NOWN + u], l[NOWN + u], o[NOWN + u]);
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][i], a.c, -m[NOWN + u]));
+                const h2 p0 = pk_rtz(p[0], p[1]);
+                const h2 p1 = pk_rtz(p[2], p[3]);
+                float ls = add_pair(p0, 0.f);
+                ls = add_pair(p1, ls);
+                l[NOWN + u] += ls;
+                const h2 z = {(_Float16)0.0f, (_Float16)0.0f};
+                h8 f;
+                if (w & 1) {  // key tile w is the upper half of k-step w/2
+                    f.s01 = z; f.s23 = z; f.s45 = p0; f.s67 = p1;
+                } else {
+                    f.s01 = p0; f.s23 = p1; f.s45 = z; f.s67 = z;
+                }
+                psh[u] = f;
+            }
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bool sh_here = NSH > 0 && kk == (w >> 1);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const h8 vf = *(const h8 *)(vt + (16 * dt + col) * St::VSTR + 32 * kk + 8 * grp);
+#pragma unroll
+                for (int k = 0; k < NOWN; ++k)
+                    o[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[k][kk], o[k][dt], 0, 0, 0);
+                if (sh_here) {
+#pragma unroll
+                    for (int u = 0; u < NSH; ++u)
+                            o[NOWN + u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, psh[u], o[NOWN + u][dt], 0, 0, 0);
+                }
+                TV_SCHED_FENCE();
+            }
+        }
+    }
+
+    // ---- own tiles: write the partial state of each query row
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) {
+        {
+            const float lt = wave_sum_16_32(l[k]);
+            const int r = 16 * tile[k] + col;
+            if (tile[k] < t_end && r < a.M) {
+                const int node = r / a.G, h = gkv * a.G + r % a.G;
+                const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
+                float *op = a.ws_o + row * D + 4 * grp;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) *(f4 *)(op + 16 * dt) = o[k][dt];
+                if (grp == 0) {
+                    a.ws_ml[2 * row] = m[k];
+                    a.ws_ml[2 * row + 1] = lt;
+                }
+            }
+        }
+    }
+
+    // ---- shared tiles: merge the four waves' partial states through LDS
+    if constexpr (NSH > 0) {
+        {
+            __syncthreads();  // every wave is done with the K/V stages
+            float *so = (float *)lds;                 // [NSH][4][16][D]
+            float *sml = so + NSH * 4 * 16 * D;       // [NSH][4][16][2]
+            static_assert(NSH * 4 * 16 * (D + 2) * 4 <= 2 * St::ELEMS * 2, "merge scratch");
+#pragma unroll
+            for (int u = 0; u < NSH; ++u) {
+                {
+                    const float lt = wave_sum_16_32(l[NOWN + u]);
+                    float *dst = so + ((u * 4 + w) * 16 + col) * D + 4 * grp;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) *(f4 *)(dst + 16 * dt) = o[NOWN + u][dt];
+                    if (grp == 0) {
+                        sml[((u * 4 + w) * 16 + col) * 2] = m[NOWN + u];
+                        sml[((u * 4 + w) * 16 + col) * 2 + 1] = lt;
+                    }
+                }
+            }
+            __syncthreads();
+            for (int u = 0; u < NSH; ++u) {
+                if (tile[NOWN + u] >= t_end) continue;
+                for (int e = tid; e < 16 * D; e += 256) {
+                    const int qr = e / D, d = e % D;
+                    const int r = 16 * tile[NOWN + u] + qr;
+                    if (r >= a.M) continue;
+                    float mw[4], mx = kNegBig;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        mw[ww] = sml[((u * 4 + ww) * 16 + qr) * 2];
+                        mx = fmaxf(mx, mw[ww]);
+                    }
+                    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        const float f = __builtin_amdgcn_exp2f(mw[ww] - mx);
+                        acc += f * so[((u * 4 + ww) * 16 + qr) * D + d];
+                        lsum += f * sml[((u * 4 + ww) * 16 + qr) * 2 + 1];
+                    }
+                    const int node = r / a.G, h = gkv * a.G + r % a.G;
+                    const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
+                    a.ws_o[row * D + d] = acc;
+                    if (d == 0) {
+                        a.ws_ml[2 * row] = mx;
+                        a.ws_ml[2 * row + 1] = lsum;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: per output row (node i, query head h), the tree ancestors' scores in
+// fp32, then the log-sum-exp combination of the split partials and the tree.
+
+struct MergeArgs {
+    const _Float16 *q;
+    const _Float16 *k_tree;
+    const _Float16 *v_tree;
+    const float *ws_o;
+    const float *ws_ml;
+    float *out;
+    int32_t NR;
+    int32_t H_q;
+    int32_t H_kv;
+    int32_t G;
+    int32_t S;
+    float c;  // scale * log2(e)
+    uint64_t anc[TV_MAX_NODES];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
+{
+    constexpr int PL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.NR) return;
+    const int i = row / a.H_q, h = row % a.H_q, g = h / a.G;
+
+    float qv[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
+
+    // tree scores; lane j keeps the score of node j
+    const uint64_t anc = a.anc[i];
+    float my_sc = -INFINITY, mt = -INFINITY;
+    for (uint64_t mm = anc; mm; mm &= mm - 1) {
+        const int j = __builtin_ctzll(mm);
+        const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
+        float part = 0.f;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], (float)kr[p], part);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        const float sj = part * a.c;
+        if (lane == j) my_sc = sj;
+        mt = fmaxf(mt, sj);
+    }
+
+    float ms = -INFINITY;
+    for (int s = lane; s < a.S; s += 64) ms = fmaxf(ms, a.ws_ml[((int64_t)s * a.NR + row) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ms = fmaxf(ms, __shfl_xor(ms, off));
+    const float mstar = fmaxf(mt, ms);
+
+    float acc[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) acc[p] = 0.f;
+    float L = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < a.S; ++s) {
+        const int64_t base = (int64_t)s * a.NR + row;
+        const float f = exp2f(a.ws_ml[2 * base] - mstar);
+        L += f * a.ws_ml[2 * base + 1];
+        const float *op = a.ws_o + base * D + lane * PL;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) acc[p] = __builtin_fmaf(f, op[p], acc[p]);
+    }
+    for (uint64_t mm = anc; mm; mm &= mm - 1) {
+        const int j = __builtin_ctzll(mm);
+        const float f = exp2f(__shfl(my_sc, j) - mstar);
+        L += f;
+        const _Float16 *vr = a.v_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) acc[p] = __builtin_fmaf(f, (float)vr[p], acc[p]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int p = 0; p < PL; ++p) a.out[(int64_t)row * D + lane * PL + p] = acc[p] * inv;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+typedef void (*split_fn)(const SplitArgs);
+
+template <int D, int KVT>
+static split_fn pick_split(int nown, int nsh)
+{
+#define TV_CASE(O, S)              \
+    if (nown == O && nsh == S) return split_kernel<D, KVT, O, S>;
+#ifdef TV_ONLY_ONE
+    TV_CASE(2, 1)
+#else
+    TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
+    TV_CASE(3, 0)
+#endif
+#undef TV_CASE
+    return nullptr;
+}
+
+static split_fn pick_split(int D, int kv, int nown, int nsh)
+{
+#ifdef TV_ONLY_ONE
+    if (kv == TV_KV_Q4_0 && D == 256) return pick_split<256, TV_KV_Q4_0>(nown, nsh);
+    return nullptr;
+#endif
+    if (kv == TV_KV_Q4_0) {
+        if (D == 64) return pick_split<64, TV_KV_Q4_0>(nown, nsh);
+        if (D == 128) return pick_split<128, TV_KV_Q4_0>(nown, nsh);
+        if (D == 256) return pick_split<256, TV_KV_Q4_0>(nown, nsh);
+    } else {
+        if (D == 64) return pick_split<64, TV_KV_F16>(nown, nsh);
+        if (D == 128) return pick_split<128, TV_KV_F16>(nown, nsh);
+        if (D == 256) return pick_split<256, TV_KV_F16>(nown, nsh);
+    }
+    return nullptr;
+}
+
+int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
+                hipStream_t stream)
+{
+    const int n = d->n_nodes, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+    const int G = Hq / Hkv;
+    const int NR = n * Hq;
+    const float c = d->scale * 1.4426950408889634f;
+    float *ws_o = (float *)ws;
+    float *ws_ml = ws_o + (size_t)plan.S * NR * D;
+
+    if (plan.S > 0) {
+        SplitArgs a;
+        a.k_cache = (const uint8_t *)p->k_cache;
+        a.v_cache = (const uint8_t *)p->v_cache;
+        a.tok_stride = d->kv_token_stride;
+        a.head_stride = d->kv_head_stride;
+        a.q = (const _Float16 *)p->q;
+        a.ws_o = ws_o;
+        a.ws_ml = ws_ml;
+        a.s0 = plan.s0;
+        a.key_end = plan.s0 + plan.R;
+        a.n_chunks = plan.n_chunks;
+        a.NR = NR;
+        a.H_q = Hq;
+        a.G = G;
+        a.M = G * n;
+        a.S = plan.S;
+        a.c = c;
+        split_fn fn = pick_split(D, d->kv_type, plan.rows.nown, plan.rows.nsh);
+        if (!fn) return TV_E_SHAPE;
+        dim3 grid(plan.S, Hkv, plan.rows.groups);
+        void *args[] = {(void *)&a};
+        if (hipLaunchKernel((const void *)fn, grid, dim3(256), args, 0, stream) != hipSuccess) return TV_E_HIP;
+    }
+
+    MergeArgs mg;
+    mg.q = (const _Float16 *)p->q;
+    mg.k_tree = (const _Float16 *)p->k_tree;
+    mg.v_tree = (const _Float16 *)p->v_tree;
+    mg.ws_o = ws_o;
+    mg.ws_ml = ws_ml;
+    mg.out = p->out;
+    mg.NR = NR;
+    mg.H_q = Hq;
+    mg.H_kv = Hkv;
+    mg.G = G;
+    mg.S = plan.S;
+    mg.c = c;
+    for (int i = 0; i < TV_MAX_NODES; ++i) mg.anc[i] = 0;
+    for (int i = 0; i < n; ++i) {
+        uint64_t mk = 0;
+        for (int u = i; u >= 0; u = d->parent[u]) mk |= 1ull << u;
+        mg.anc[i] = mk;
+    }
+    dim3 mgrid((NR + 3) / 4);
+    if (D == 64)
+        hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, mg);
+    else if (D == 128)
+        hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, mg);
+    else
+        hipLaunchKernelGGL(merge_kernel<256>, mgrid, dim3(256), 0, stream, mg);
+    if (hipGetLastError() != hipSuccess) return TV_E_HIP;
+    return TV_OK;
+}
+
+}  // namespace tv

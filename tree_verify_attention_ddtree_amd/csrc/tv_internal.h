@@ -1,0 +1,52 @@
+// Internal declarations shared by the HIP sources of libtv.so (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tree_verify.h"
+
+namespace tv {
+
+// Keys per pipeline stage of the split kernel.
+constexpr int kChunk = 64;
+// Query tiles (16 rows each) a wave may hold: own tiles + shared tiles.
+constexpr int kMaxSlots = 3;
+
+// How the packed query rows of one KV head are cut into row groups and how a
+// group's 16-row tiles are spread over the 4 waves of a workgroup.
+struct RowPlan {
+    int tiles;   // ceil(M / 16), M = G * n_nodes
+    int groups;  // row groups (grid z)
+    int nown;    // max own tiles per wave over groups
+    int nsh;     // max shared tiles per group
+};
+
+// Per-group tile roles: a group of Tg tiles gives every wave Tg/4 own tiles;
+// of the Tg%4 left over, 1 or 2 are shared (each split by keys over the four
+// waves) and 3 become one more own tile for waves 0..2.
+inline void group_roles(int Tg, int *own_max, int *sh)
+{
+    const int a = Tg / 4, r = Tg % 4;
+    if (r == 3) {
+        *own_max = a + 1;
+        *sh = 0;
+    } else {
+        *own_max = a;
+        *sh = r;
+    }
+}
+
+struct SplitPlan {
+    RowPlan rows;
+    int64_t s0;       // first cache row in the window
+    int64_t R;        // cache rows in the window
+    int64_t n_chunks; // ceil(R / kChunk)
+    int S;            // key-range splits per (KV head, row group)
+};
+
+int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out);
+size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p);
+int device_cu_count(int *n_cu);
+
+}  // namespace tv
