@@ -40,8 +40,22 @@ def parse():
     ap.add_argument("--kv", default="q4_0", choices=["q4_0", "f16"])
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9, help="KV bytes the copies span at least")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="oracle output rows timed for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=552, help="oracle output rows timed for the CPU baseline")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="only copy a device buffer of this many bytes --steps times (HBM counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of known size, the yardstick that scales
+    the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    import torch
+    src = torch.ones(int(nbytes) // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "steps": steps}))
 
 
 def main():
@@ -49,6 +63,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import torch
 

@@ -12,8 +12,8 @@
 // (order-preserving float code << 32 | ~index) so that the maximum key is the
 // largest value with the smallest index; NaN maps to the lowest code and -0 to
 // the code of +0.
-// Kernel 2 (finish_walk): one wave. Reduces the slices of every row, writes
-// the argmax, then one lane walks the tree (n <= 64).
+// Kernel 2 (finish_walk): one wave, lane i = node i: reduces the slices of
+// row i, then finds the accepted path with wave-wide pointer jumping.
 
 #include "tv_internal.h"
 
@@ -90,63 +90,101 @@ struct WalkArgs {
     int32_t tokens[TV_MAX_NODES];
 };
 
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src)
+{
+    const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One wave; lane i stands for tree node i.
+//   1. a[i]: lane i reduces the slice maxima of row i.
+//   2. Pointer jumping over parents (6 rounds cover depth 63): depth, whether
+//      every edge of the root path matches (child token == parent's argmax),
+//      and the ancestor-or-self bitmask.
+//   3. The deepest matched nodes mark their root paths; the descent from the
+//      root takes, at every level, the smallest child on a marked path, which
+//      is the lexicographically smallest of the longest accepted paths.
 __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
 {
-    __shared__ int32_t am[TV_MAX_NODES];
     const int lane = threadIdx.x;
-    // one row per iteration, slices spread over the wave
-    for (int i = 0; i < a.n; ++i) {
-        uint64_t b = 0;
-        for (int s = lane; s < a.n_slices; s += 64) b = umax64(b, a.part[(int64_t)i * a.n_slices + s]);
-        b = wave_umax64(b);
-        if (lane == 0) {
-            const int32_t idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFu));
-            am[i] = idx;
-            a.argmax_out[i] = idx;
-        }
-    }
-    __syncthreads();
-    if (lane != 0) return;
-    // matched: node i lies on an accepted path from the root
-    bool matched[TV_MAX_NODES];
-    int depth[TV_MAX_NODES], reach[TV_MAX_NODES];
-    matched[0] = true;
-    depth[0] = 0;
-    for (int i = 1; i < a.n; ++i) {
-        const int p = a.parent[i];
-        depth[i] = depth[p] + 1;
-        matched[i] = matched[p] && a.tokens[i] == am[p];
-    }
-    // reach[u]: deepest matched depth below (or at) matched node u
-    for (int i = 0; i < a.n; ++i) reach[i] = matched[i] ? depth[i] : -1;
-    for (int i = a.n - 1; i > 0; --i)
-        if (matched[i] && reach[i] > reach[a.parent[i]]) reach[a.parent[i]] = reach[i];
-    // descend: at every node take the smallest child that still reaches the
-    // deepest matched depth
-    int path[TV_MAX_NODES];
-    int len = 0, u = 0;
-    path[len++] = 0;
-    for (;;) {
-        int next = -1;
-        for (int c = u + 1; c < a.n; ++c)
-            if (a.parent[c] == u && matched[c] && reach[c] == reach[0]) {
-                next = c;
-                break;
-            }
-        if (next < 0) break;
-        path[len++] = next;
-        u = next;
-    }
     const int n = a.n;
+    int par = -1, tok = -1;
+#pragma unroll
+    for (int i = 0; i < TV_MAX_NODES; ++i)
+        if (lane == i) {
+            par = a.parent[i];
+            tok = a.tokens[i];
+        }
+    const bool live = lane < n;
+
+    int am = 0;
+    if (live) {
+        uint64_t b = 0;
+        const uint64_t *pr = a.part + (int64_t)lane * a.n_slices;
+        for (int s = 0; s < a.n_slices; ++s) b = umax64(b, pr[s]);
+        am = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFu));
+        a.argmax_out[lane] = am;
+    }
+
+    const int p0 = (live && lane > 0) ? par : lane;  // root and dead lanes point to themselves
+    const int am_parent = __shfl(am, p0);
+    bool ok = !live ? false : (lane == 0 ? true : tok == am_parent);
+    int nxt = p0;
+    int depth = (live && lane > 0) ? 1 : 0;
+    uint64_t msk = 1ull << lane;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const bool ok_n = __shfl((int)ok, nxt) != 0;
+        const int d_n = __shfl(depth, nxt);
+        const uint64_t m_n = shfl64(msk, nxt);
+        const int nxt_n = __shfl(nxt, nxt);
+        if (nxt != lane) {
+            ok = ok && ok_n;
+            depth += d_n;
+            msk |= m_n;
+        }
+        nxt = nxt_n;
+    }
+    const bool matched = live && ok;
+    int best = matched ? depth : -1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
+    uint64_t onpath = (matched && depth == best) ? msk : 0ull;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) onpath |= shfl64(onpath, lane ^ off);
+
+    // descent; lane k records the k-th node of the path
+    int u = 0, len = 1, mypath = lane == 0 ? 0 : -1;
+    for (;;) {
+        const uint64_t cand = __builtin_amdgcn_ballot_w64(live && lane > 0 && par == u && ((onpath >> lane) & 1));
+        if (!cand) break;
+        u = __builtin_ctzll(cand);
+        if (lane == len) mypath = u;
+        ++len;
+    }
     const int n_acc = len - 1;
-    const int bonus = am[path[len - 1]];
-    int32_t *res = a.result_out;
-    for (int k = 0; k < 2 + 2 * n; ++k) res[k] = -1;
-    res[0] = n_acc;
-    res[1] = bonus;
-    for (int k = 0; k < len; ++k) res[2 + k] = path[k];
-    for (int k = 1; k < len; ++k) res[2 + n + k - 1] = a.tokens[path[k]];
-    res[2 + n + n_acc] = bonus;
+    const int bonus = __shfl(am, u);
+    // every output position is written exactly once; the shuffles run with
+    // all lanes active
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int pos = lane + 64 * r;
+        const int jp = pos - 2;      // index into the path
+        const int je = pos - 2 - n;  // index into the emitted tokens
+        const int pj = __shfl(mypath, (jp >= 0 && jp < 64) ? jp : 0);
+        const int pe = __shfl(mypath, (je + 1 >= 0 && je + 1 < 64) ? je + 1 : 0);
+        const int te = __shfl(tok, (pe >= 0 && pe < 64) ? pe : 0);
+        int v;
+        if (pos == 0)
+            v = n_acc;
+        else if (pos == 1)
+            v = bonus;
+        else if (pos < 2 + n)
+            v = jp <= n_acc ? pj : -1;
+        else
+            v = je < n_acc ? te : (je == n_acc ? bonus : -1);
+        if (pos < 2 + 2 * n) a.result_out[pos] = v;
+    }
 }
 
 static int64_t n_slices_for(int vocab) { return ((int64_t)vocab + kSliceFloats - 1) / kSliceFloats; }

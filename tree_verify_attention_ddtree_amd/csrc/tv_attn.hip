@@ -424,23 +424,29 @@ split_kernel(const SplitArgs a)
             for (int kt = 0; kt < 4; ++kt) sacc[k][kt] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
+        // K fragments of block bb+1 are read from LDS while the MFMAs of
+        // block bb run (one block of lookahead, 5 fragments per block).
+        h8 kf[2][5];
+        auto kload = [&](int bb, h8(&f)[5]) {
             if constexpr (NOWN > 0) {
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const h8 kf = *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
-#pragma unroll
-                    for (int k = 0; k < NOWN; ++k)
-                        sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[k][bb], sacc[k][kt], 0, 0, 0);
-                }
+                for (int kt = 0; kt < 4; ++kt)
+                    f[kt] = *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
             }
-            if constexpr (NSH > 0) {
-                const h8 kf = *(const h8 *)(ks + (16 * w + col) * St::KSTR + 32 * bb + 8 * grp);
+            if constexpr (NSH > 0) f[4] = *(const h8 *)(ks + (16 * w + col) * St::KSTR + 32 * bb + 8 * grp);
+        };
+        kload(0, kf[0]);
 #pragma unroll
-                for (int u = 0; u < NSH; ++u)
-                    ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[NOWN + u][bb], ssh[u], 0, 0, 0);
-            }
+        for (int bb = 0; bb < NB; ++bb) {
+            if (bb + 1 < NB) kload(bb + 1, kf[(bb + 1) & 1]);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int k = 0; k < NOWN; ++k)
+                    sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[bb & 1][kt], qf[k][bb], sacc[k][kt], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < NSH; ++u)
+                ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[bb & 1][4], qf[NOWN + u][bb], ssh[u], 0, 0, 0);
             TV_SCHED_FENCE();
         }
 
@@ -520,23 +526,40 @@ split_kernel(const SplitArgs a)
             }
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T; V fragments in groups of 4 with one group of
+        // lookahead. Fragment idx covers k-step kk = idx / NDT, d-tile idx % NDT.
+        constexpr int NG = 2 * NDT / 4;
+        h8 vf[2][4];
+        auto vload = [&](int g, h8(&f)[4]) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+            for (int j = 0; j < 4; ++j) {
+                const int idx = 4 * g + j, kk = idx / NDT, dt = idx % NDT;
+                f[j] = *(const h8 *)(vt + (16 * dt + col) * St::VSTR + 32 * kk + 8 * grp);
+            }
+        };
+        vload(0, vf[0]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) vload(g + 1, vf[(g + 1) & 1]);
+            const int kk = (4 * g) / NDT;
             const bool sh_here = NSH > 0 && kk == (w >> 1);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const h8 vf = *(const h8 *)(vt + (16 * dt + col) * St::VSTR + 32 * kk + 8 * grp);
+            for (int j = 0; j < 4; ++j) {
+                const int dt = (4 * g + j) % NDT;
 #pragma unroll
                 for (int k = 0; k < NOWN; ++k)
-                    o[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[k][kk], o[k][dt], 0, 0, 0);
-                if (sh_here) {
+                    o[k][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][j], pf[k][kk], o[k][dt], 0, 0, 0);
+            }
+            if (sh_here) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int dt = (4 * g + j) % NDT;
 #pragma unroll
                     for (int u = 0; u < NSH; ++u)
-                            o[NOWN + u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, psh[u], o[NOWN + u][dt], 0, 0, 0);
+                        o[NOWN + u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][j], psh[u], o[NOWN + u][dt], 0, 0, 0);
                 }
-                TV_SCHED_FENCE();
             }
+            TV_SCHED_FENCE();
         }
     }
 
@@ -633,65 +656,91 @@ struct MergeArgs {
     uint64_t anc[TV_MAX_NODES];
 };
 
+// One workgroup per output row. Thread t owns the 4 output values of d-quad
+// t % (D/4) for the splits s = t / (D/4) (mod D-quad groups); the groups are
+// summed through LDS at the end. Wave 0 scores the tree ancestors first.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 {
-    constexpr int PL = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.NR) return;
+    constexpr int QD = D / 4;       // d-quads per row
+    constexpr int NGR = 256 / QD;   // split groups
+    constexpr int PL = D / 64;      // values per lane for the tree dot products
+    __shared__ float sc[TV_MAX_NODES];
+    __shared__ float red[256];
+    __shared__ __attribute__((aligned(16))) float acc_s[NGR][D];
+    __shared__ float l_s[NGR];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int row = blockIdx.x;
     const int i = row / a.H_q, h = row % a.H_q, g = h / a.G;
-
-    float qv[PL];
-#pragma unroll
-    for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
-
-    // tree scores; lane j keeps the score of node j
     const uint64_t anc = a.anc[i];
-    float my_sc = -INFINITY, mt = -INFINITY;
-    for (uint64_t mm = anc; mm; mm &= mm - 1) {
-        const int j = __builtin_ctzll(mm);
-        const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
-        float part = 0.f;
+
+    // tree scores (wave 0), kept in LDS
+    float mt = -INFINITY;
+    if (w == 0) {
+        float qv[PL];
 #pragma unroll
-        for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], (float)kr[p], part);
+        for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
+        for (uint64_t mm = anc; mm; mm &= mm - 1) {
+            const int j = __builtin_ctzll(mm);
+            const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
+            float part = 0.f;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        const float sj = part * a.c;
-        if (lane == j) my_sc = sj;
-        mt = fmaxf(mt, sj);
+            for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], (float)kr[p], part);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+            const float sj = part * a.c;
+            if (lane == 0) sc[j] = sj;
+            mt = fmaxf(mt, sj);
+        }
     }
+    // max over the split maxima and the tree
+    float mx = w == 0 ? mt : -INFINITY;
+    for (int s = t; s < a.S; s += 256) mx = fmaxf(mx, a.ws_ml[((int64_t)s * a.NR + row) * 2]);
+    red[t] = mx;
+    __syncthreads();
+    for (int k = 128; k >= 1; k >>= 1) {
+        if (t < k) red[t] = fmaxf(red[t], red[t + k]);
+        __syncthreads();
+    }
+    const float mstar = red[0];
 
-    float ms = -INFINITY;
-    for (int s = lane; s < a.S; s += 64) ms = fmaxf(ms, a.ws_ml[((int64_t)s * a.NR + row) * 2]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ms = fmaxf(ms, __shfl_xor(ms, off));
-    const float mstar = fmaxf(mt, ms);
-
-    float acc[PL];
-#pragma unroll
-    for (int p = 0; p < PL; ++p) acc[p] = 0.f;
+    const int dq = t % QD, sg = t / QD;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
 #pragma unroll 4
-    for (int s = 0; s < a.S; ++s) {
+    for (int s = sg; s < a.S; s += NGR) {
         const int64_t base = (int64_t)s * a.NR + row;
         const float f = exp2f(a.ws_ml[2 * base] - mstar);
-        L += f * a.ws_ml[2 * base + 1];
-        const float *op = a.ws_o + base * D + lane * PL;
-#pragma unroll
-        for (int p = 0; p < PL; ++p) acc[p] = __builtin_fmaf(f, op[p], acc[p]);
+        L = __builtin_fmaf(f, a.ws_ml[2 * base + 1], L);
+        const f4 o = *(const f4 *)(a.ws_o + base * D + 4 * dq);
+        acc += f * o;
     }
-    for (uint64_t mm = anc; mm; mm &= mm - 1) {
-        const int j = __builtin_ctzll(mm);
-        const float f = exp2f(__shfl(my_sc, j) - mstar);
-        L += f;
-        const _Float16 *vr = a.v_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
-#pragma unroll
-        for (int p = 0; p < PL; ++p) acc[p] = __builtin_fmaf(f, (float)vr[p], acc[p]);
+    if (sg == 0) {
+        for (uint64_t mm = anc; mm; mm &= mm - 1) {
+            const int j = __builtin_ctzll(mm);
+            const float f = exp2f(sc[j] - mstar);
+            L += f;
+            const _Float16 *vr = a.v_tree + ((int64_t)j * a.H_kv + g) * D + 4 * dq;
+            acc.x = __builtin_fmaf(f, (float)vr[0], acc.x);
+            acc.y = __builtin_fmaf(f, (float)vr[1], acc.y);
+            acc.z = __builtin_fmaf(f, (float)vr[2], acc.z);
+            acc.w = __builtin_fmaf(f, (float)vr[3], acc.w);
+        }
     }
-    const float inv = 1.0f / L;
+    *(f4 *)&acc_s[sg][4 * dq] = acc;
+    if (dq == 0) l_s[sg] = L;
+    __syncthreads();
+    if (t < QD) {
+        f4 sum = *(const f4 *)&acc_s[0][4 * t];
+        float Ls = l_s[0];
 #pragma unroll
-    for (int p = 0; p < PL; ++p) a.out[(int64_t)row * D + lane * PL + p] = acc[p] * inv;
+        for (int k = 1; k < NGR; ++k) {
+            sum += *(const f4 *)&acc_s[k][4 * t];
+            Ls += l_s[k];
+        }
+        *(f4 *)(a.out + (int64_t)row * D + 4 * t) = sum * (1.0f / Ls);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -786,7 +835,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         for (int u = i; u >= 0; u = d->parent[u]) mk |= 1ull << u;
         mg.anc[i] = mk;
     }
-    dim3 mgrid((NR + 3) / 4);
+    dim3 mgrid(NR);
     if (D == 64)
         hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, mg);
     else if (D == 128)
