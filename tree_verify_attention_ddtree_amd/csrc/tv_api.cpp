@@ -48,6 +48,8 @@ static int check_desc(const tv_attn_desc *d)
         const int64_t row = d->kv_type == TV_KV_Q4_0 ? (int64_t)d->head_dim / 32 * 18 : (int64_t)d->head_dim * 2;
         const int64_t al = d->kv_type == TV_KV_Q4_0 ? 4 : 16;
         if (d->kv_token_stride < row || d->kv_head_stride < 0) return TV_E_SHAPE;
+        // per-thread row offsets inside a 64-row chunk are 32-bit
+        if (d->kv_token_stride > ((int64_t)1 << 24)) return TV_E_SHAPE;
         if (d->kv_token_stride % al || d->kv_head_stride % al) return TV_E_ALIGN;
     }
     return TV_OK;
@@ -84,7 +86,9 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     if (rc) return rc;
     out->s0 = (d->window > 0 && d->n_ctx > d->window) ? d->n_ctx - d->window : 0;
     out->R = d->n_ctx - out->s0;
-    out->n_chunks = (out->R + kChunk - 1) / kChunk;
+    // whole chunks go to the split kernel; the last R % kChunk rows of the
+    // window are attended by the merge kernel together with the tree
+    out->n_chunks = out->R / kChunk;
     if (out->n_chunks == 0) {
         out->S = 0;
         return TV_OK;

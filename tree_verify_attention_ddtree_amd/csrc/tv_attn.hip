@@ -31,101 +31,11 @@
 //     only moves when a chunk's max exceeds it by more than 2^8), P rounded to
 //     fp16 and its row sums taken from the rounded values.
 
-#include <math.h>
 #include <string.h>
 
-#include "tv_internal.h"
+#include "tv_split_common.h"
 
 namespace tv {
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32;
-
-// Keeps the scheduler from hoisting every LDS fragment load of an unrolled
-// loop to its top, which would need a register per fragment.
-#ifndef TV_NO_FENCE
-#define TV_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define TV_SCHED_FENCE()
-#endif
-
-constexpr float kTau = 8.0f;
-constexpr float kNegBig = -1.0e30f;
-
-struct SplitArgs {
-    const uint8_t *k_cache;
-    const uint8_t *v_cache;
-    int64_t tok_stride;
-    int64_t head_stride;
-    const _Float16 *q;
-    float *ws_o;   // [S][NR][D] unnormalised partial outputs
-    float *ws_ml;  // [S][NR][2] running max (log2 units) and row sum
-    int64_t s0;
-    int64_t key_end;
-    int64_t n_chunks;
-    int32_t NR;  // n * H_q
-    int32_t H_q;
-    int32_t G;
-    int32_t M;  // G * n
-    int32_t S;
-    float c;  // scale * log2(e)
-};
-
-typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ h2 as_h2(u32 x) { return __builtin_bit_cast(h2, x); }
-
-// fp32 pair -> fp16 pair (round toward zero), one instruction
-__device__ __forceinline__ h2 pk_rtz(float a, float b)
-{
-    return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// acc + p.x + p.y in fp32 (exact products with 1, fp32 sums)
-__device__ __forceinline__ float add_pair(h2 p, float acc)
-{
-    const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, p), one, acc, false);
-}
-
-// 8 Q4_0 codes packed in one dword (code bytes 4k..4k+3 of a block) -> the
-// exact values code - 8 as four fp16 pairs: [0] = elements (4k, 4k+2),
-// [1] = (4k+1, 4k+3), [2] = (4k+16, 4k+18), [3] = (4k+17, 4k+19).
-// 0x6400 | c is fp16 1024 + c; 0x6400 | (c << 4) is 1024 + 16 c.
-__device__ __forceinline__ void q4_unpack(u32 x, h2 v[4])
-{
-    const u32 y = x >> 8;
-    const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    v[0] = as_h2((x & 0x000F000Fu) | 0x64006400u) - off;
-    v[1] = as_h2((y & 0x000F000Fu) | 0x64006400u) - off;
-    v[2] = __builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
-    v[3] = __builtin_elementwise_fma(as_h2((y & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
-}
-
-// Position of chunk key kappa (0..63) in a transposed V row: inside each group
-// of 32 keys, the 8 keys a lane group of the PV MFMA consumes are contiguous.
-__device__ __forceinline__ int vpos(int kappa)
-{
-    return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
-}
-
-template <int D, int KVT>
-struct Stage {
-    static constexpr int NB = D / 32;   // 32-wide blocks per row
-    static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
-    static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
-    static constexpr int VSTR = kChunk + 8;  // V^T row stride in LDS (halves)
-    static constexpr int KELEMS = kChunk * KSTR;
-    static constexpr int VELEMS = D * VSTR;
-    static constexpr int ELEMS = KELEMS + VELEMS;
-    // raw registers per thread for the next chunk
-    static constexpr int RAW = KVT == TV_KV_Q4_0 ? NK * 5 : NK * 16;
-};
 
 // Thread t of the 256 handles K (t < 128) or V (t >= 128), NK consecutive
 // keys of the chunk and one 32-value block of those rows.
@@ -140,28 +50,18 @@ __device__ __forceinline__ void load_raw(const SplitArgs &a, int gkv, int64_t kb
     for (int kk = 0; kk < St::NK; ++kk) {
         const int64_t row = kbase + key0 + kk;
         if constexpr (KVT == TV_KV_Q4_0) {
-            if (row < a.key_end) {
-                const u32 *p = (const u32 *)(base + row * a.tok_stride + ((18 * b) & ~3));
+            const u32 *p = (const u32 *)(base + row * a.tok_stride + ((18 * b) & ~3));
 #pragma unroll
-                for (int j = 0; j < 5; ++j) raw[kk * 5 + j] = p[j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 5; ++j) raw[kk * 5 + j] = 0u;
-            }
+            for (int j = 0; j < 5; ++j) raw[kk * 5 + j] = p[j];
         } else {
-            if (row < a.key_end) {
-                const uint4 *p = (const uint4 *)(base + row * a.tok_stride + 64 * b);
+            const uint4 *p = (const uint4 *)(base + row * a.tok_stride + 64 * b);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 t = p[j];
-                    raw[kk * 16 + 4 * j + 0] = t.x;
-                    raw[kk * 16 + 4 * j + 1] = t.y;
-                    raw[kk * 16 + 4 * j + 2] = t.z;
-                    raw[kk * 16 + 4 * j + 3] = t.w;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) raw[kk * 16 + j] = 0u;
+            for (int j = 0; j < 4; ++j) {
+                const uint4 t = p[j];
+                raw[kk * 16 + 4 * j + 0] = t.x;
+                raw[kk * 16 + 4 * j + 1] = t.y;
+                raw[kk * 16 + 4 * j + 2] = t.z;
+                raw[kk * 16 + 4 * j + 3] = t.w;
             }
         }
     }
@@ -292,36 +192,6 @@ __device__ __forceinline__ void store_stage(const u32 *raw, _Float16 *ks, _Float
     }
 }
 
-__device__ __forceinline__ float wave_max_16_32(float x)
-{
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum_16_32(float x)
-{
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
-
-// Rescale one query tile's state when its chunk max mnew exceeds the running
-// max by more than kTau anywhere in the wave.
-template <int NDT>
-__device__ __forceinline__ void maybe_rescale(float mnew, float &m, float &l, f4 (&o)[NDT])
-{
-    const bool need = mnew > m + kTau;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mm = fmaxf(m, mnew);
-        const float f = __builtin_amdgcn_exp2f(m - mm);
-        l *= f;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
-        m = mm;
-    }
-}
-
 template <int D, int KVT, int NOWN, int NSH>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 split_kernel(const SplitArgs a)
@@ -339,47 +209,18 @@ split_kernel(const SplitArgs a)
     const int col = lane & 15, grp = lane >> 4;
     const int split = blockIdx.x, gkv = blockIdx.y, rg = blockIdx.z;
 
-    // ---- tiles of this row group: own tile k of wave w is t0 + 4k + w, shared
-    // tile u is t0 + 4*NOWN + u; tiles at or past t0 + Tg are padding (zero
-    // queries, results dropped), so every wave runs the same instructions.
-    const int T = (a.M + 15) / 16;
-    const int RG = gridDim.z;
-    const int tb = T / RG, te = T % RG;
-    const int Tg = tb + (rg < te ? 1 : 0);
-    const int t0 = rg * tb + (rg < te ? rg : te);
-    const int t_end = t0 + Tg;
+    TileMap tm;
+    tm.init(a.M, rg, gridDim.z);
+    const int t_end = tm.t_end;
     int tile[NS];
 #pragma unroll
-    for (int k = 0; k < NOWN; ++k) tile[k] = t0 + 4 * k + w;
+    for (int k = 0; k < NOWN; ++k) tile[k] = tm.t0 + 4 * k + w;
 #pragma unroll
-    for (int u = 0; u < NSH; ++u) tile[NOWN + u] = t0 + 4 * NOWN + u;
+    for (int u = 0; u < NSH; ++u) tile[NOWN + u] = tm.t0 + 4 * NOWN + u;
 
-    // ---- Q fragments (B operand of S^T = K Q^T), zero for padding rows
     h8 qf[NS][NB];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-        const int r = 16 * tile[k] + col;
-        if (tile[k] < t_end && r < a.M) {
-            const int node = r / a.G, h = gkv * a.G + r % a.G;
-            const _Float16 *qr = a.q + ((int64_t)node * a.H_q + h) * D;
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                if constexpr (KVT == TV_KV_Q4_0) {
-                    const h4 lo = *(const h4 *)(qr + 32 * bb + 4 * grp);
-                    const h4 hi = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
-                    h8 f;
-                    f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
-                    f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
-                    qf[k][bb] = f;
-                } else {
-                    qf[k][bb] = *(const h8 *)(qr + 32 * bb + 8 * grp);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) qf[k][bb] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
+    for (int k = 0; k < NS; ++k) load_q_frags<D, KVT>(a, gkv, tile[k], t_end, col, grp, qf[k]);
 
     // The Q fragments are read only as MFMA B operands, which may come from
     // AGPRs; parking them there leaves the VGPRs to the accumulators.
@@ -412,8 +253,6 @@ split_kernel(const SplitArgs a)
         if (c + 1 < c_end) load_raw<D, KVT>(a, gkv, a.s0 + (c + 1) * kChunk, tid, raw);
         __syncthreads();
 
-        const int64_t kbase = a.s0 + c * kChunk;
-        const bool ragged = kbase + kChunk > a.key_end;
 
         // ---- S^T tiles: 4 key tiles x own slots, key tile w x shared slots
         f4 sacc[NOWN > 0 ? NOWN : 1][4];
@@ -462,7 +301,6 @@ split_kernel(const SplitArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float v = sacc[k][kt][i];
-                        if (ragged && kbase + 16 * kt + 4 * grp + i >= a.key_end) v = -INFINITY;
                         sacc[k][kt][i] = v;
                         mx = fmaxf(mx, v);
                     }
@@ -501,7 +339,6 @@ split_kernel(const SplitArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float v = ssh[u][i];
-                    if (ragged && kbase + 16 * w + 4 * grp + i >= a.key_end) v = -INFINITY;
                     ssh[u][i] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -563,77 +400,8 @@ split_kernel(const SplitArgs a)
         }
     }
 
-    // ---- own tiles: write the partial state of each query row
-#pragma unroll
-    for (int k = 0; k < NOWN; ++k) {
-        {
-            const float lt = wave_sum_16_32(l[k]);
-            const int r = 16 * tile[k] + col;
-            if (tile[k] < t_end && r < a.M) {
-                const int node = r / a.G, h = gkv * a.G + r % a.G;
-                const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-                float *op = a.ws_o + row * D + 4 * grp;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) *(f4 *)(op + 16 * dt) = o[k][dt];
-                if (grp == 0) {
-                    a.ws_ml[2 * row] = m[k];
-                    a.ws_ml[2 * row + 1] = lt;
-                }
-            }
-        }
-    }
-
-    // ---- shared tiles: merge the four waves' partial states through LDS
-    if constexpr (NSH > 0) {
-        {
-            __syncthreads();  // every wave is done with the K/V stages
-            float *so = (float *)lds;                 // [NSH][4][16][D]
-            float *sml = so + NSH * 4 * 16 * D;       // [NSH][4][16][2]
-            static_assert(NSH * 4 * 16 * (D + 2) * 4 <= 2 * St::ELEMS * 2, "merge scratch");
-#pragma unroll
-            for (int u = 0; u < NSH; ++u) {
-                {
-                    const float lt = wave_sum_16_32(l[NOWN + u]);
-                    float *dst = so + ((u * 4 + w) * 16 + col) * D + 4 * grp;
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) *(f4 *)(dst + 16 * dt) = o[NOWN + u][dt];
-                    if (grp == 0) {
-                        sml[((u * 4 + w) * 16 + col) * 2] = m[NOWN + u];
-                        sml[((u * 4 + w) * 16 + col) * 2 + 1] = lt;
-                    }
-                }
-            }
-            __syncthreads();
-            for (int u = 0; u < NSH; ++u) {
-                if (tile[NOWN + u] >= t_end) continue;
-                for (int e = tid; e < 16 * D; e += 256) {
-                    const int qr = e / D, d = e % D;
-                    const int r = 16 * tile[NOWN + u] + qr;
-                    if (r >= a.M) continue;
-                    float mw[4], mx = kNegBig;
-#pragma unroll
-                    for (int ww = 0; ww < 4; ++ww) {
-                        mw[ww] = sml[((u * 4 + ww) * 16 + qr) * 2];
-                        mx = fmaxf(mx, mw[ww]);
-                    }
-                    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-                    for (int ww = 0; ww < 4; ++ww) {
-                        const float f = __builtin_amdgcn_exp2f(mw[ww] - mx);
-                        acc += f * so[((u * 4 + ww) * 16 + qr) * D + d];
-                        lsum += f * sml[((u * 4 + ww) * 16 + qr) * 2 + 1];
-                    }
-                    const int node = r / a.G, h = gkv * a.G + r % a.G;
-                    const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-                    a.ws_o[row * D + d] = acc;
-                    if (d == 0) {
-                        a.ws_ml[2 * row] = mx;
-                        a.ws_ml[2 * row + 1] = lsum;
-                    }
-                }
-            }
-        }
-    }
+    static_assert(NSH * 4 * 16 * (D + 2) * 4 <= 2 * St::ELEMS * 2, "merge scratch");
+    write_partials<D, NOWN, NSH>(a, lds, 2 * St::ELEMS * 2, tid, w, col, grp, gkv, split, t_end, tile, o, m, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -653,8 +421,39 @@ struct MergeArgs {
     int32_t G;
     int32_t S;
     float c;  // scale * log2(e)
+    // cache rows [tail_begin, tail_end) of the window that do not fill a
+    // whole chunk of the split kernel
+    const uint8_t *k_cache;
+    const uint8_t *v_cache;
+    int64_t tok_stride;
+    int64_t head_stride;
+    int64_t tail_begin;
+    int32_t n_tail;
+    int32_t kv_type;
     uint64_t anc[TV_MAX_NODES];
 };
+
+// Values d0 .. d0+n-1 (n <= 4, inside one 32-wide block) of one cache row,
+// decoded exactly in fp32.
+template <int N>
+__device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, int d0, float (&out)[N])
+{
+    if (kv_type == TV_KV_Q4_0) {
+        const uint8_t *blk = row + 18 * (d0 / 32);
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[0] | (blk[1] << 8)));
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            const int e = (d0 + p) % 32;
+            const int byte = blk[2 + (e % 16)];
+            const int code = e < 16 ? (byte & 15) : (byte >> 4);
+            out[p] = s * (float)(code - 8);
+        }
+    } else {
+        const _Float16 *h = (const _Float16 *)row + d0;
+#pragma unroll
+        for (int p = 0; p < N; ++p) out[p] = (float)h[p];
+    }
+}
 
 // One workgroup per output row. Thread t owns the 4 output values of d-quad
 // t % (D/4) for the splits s = t / (D/4) (mod D-quad groups); the groups are
@@ -666,6 +465,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     constexpr int NGR = 256 / QD;   // split groups
     constexpr int PL = D / 64;      // values per lane for the tree dot products
     __shared__ float sc[TV_MAX_NODES];
+    __shared__ float stl[kChunk];
     __shared__ float red[256];
     __shared__ __attribute__((aligned(16))) float acc_s[NGR][D];
     __shared__ float l_s[NGR];
@@ -694,8 +494,28 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
             mt = fmaxf(mt, sj);
         }
     }
-    // max over the split maxima and the tree
-    float mx = w == 0 ? mt : -INFINITY;
+    // tail cache rows (wave 1)
+    const uint8_t *kh = a.k_cache + (int64_t)g * a.head_stride;
+    const uint8_t *vh = a.v_cache + (int64_t)g * a.head_stride;
+    if (w == 1 && a.n_tail > 0) {
+        float qv[PL];
+#pragma unroll
+        for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
+        for (int j = 0; j < a.n_tail; ++j) {
+            float kv[PL];
+            cache_values<PL>(kh + (a.tail_begin + j) * a.tok_stride, a.kv_type, lane * PL, kv);
+            float part = 0.f;
+#pragma unroll
+            for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], kv[p], part);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+            const float sj = part * a.c;
+            if (lane == 0) stl[j] = sj;
+            mt = fmaxf(mt, sj);
+        }
+    }
+    // max over the split maxima, the tree and the tail
+    float mx = (w == 0 || w == 1) ? mt : -INFINITY;
     for (int s = t; s < a.S; s += 256) mx = fmaxf(mx, a.ws_ml[((int64_t)s * a.NR + row) * 2]);
     red[t] = mx;
     __syncthreads();
@@ -728,6 +548,18 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
             acc.w = __builtin_fmaf(f, (float)vr[3], acc.w);
         }
     }
+    if (sg == 1) {
+        for (int j = 0; j < a.n_tail; ++j) {
+            const float f = exp2f(stl[j] - mstar);
+            L += f;
+            float vv[4];
+            cache_values<4>(vh + (a.tail_begin + j) * a.tok_stride, a.kv_type, 4 * dq, vv);
+            acc.x = __builtin_fmaf(f, vv[0], acc.x);
+            acc.y = __builtin_fmaf(f, vv[1], acc.y);
+            acc.z = __builtin_fmaf(f, vv[2], acc.z);
+            acc.w = __builtin_fmaf(f, vv[3], acc.w);
+        }
+    }
     *(f4 *)&acc_s[sg][4 * dq] = acc;
     if (dq == 0) l_s[sg] = L;
     __syncthreads();
@@ -746,33 +578,22 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 // ---------------------------------------------------------------------------
 // Host side.
 
-typedef void (*split_fn)(const SplitArgs);
 
 template <int D, int KVT>
 static split_fn pick_split(int nown, int nsh)
 {
 #define TV_CASE(O, S)              \
     if (nown == O && nsh == S) return split_kernel<D, KVT, O, S>;
-#ifdef TV_ONLY_ONE
-    TV_CASE(2, 1)
-#else
     TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
     TV_CASE(3, 0)
-#endif
 #undef TV_CASE
     return nullptr;
 }
 
 static split_fn pick_split(int D, int kv, int nown, int nsh)
 {
-#ifdef TV_ONLY_ONE
-    if (kv == TV_KV_Q4_0 && D == 256) return pick_split<256, TV_KV_Q4_0>(nown, nsh);
-    return nullptr;
-#endif
     if (kv == TV_KV_Q4_0) {
-        if (D == 64) return pick_split<64, TV_KV_Q4_0>(nown, nsh);
-        if (D == 128) return pick_split<128, TV_KV_Q4_0>(nown, nsh);
-        if (D == 256) return pick_split<256, TV_KV_Q4_0>(nown, nsh);
+        return pick_split_q4(D, nown, nsh);
     } else {
         if (D == 64) return pick_split<64, TV_KV_F16>(nown, nsh);
         if (D == 128) return pick_split<128, TV_KV_F16>(nown, nsh);
@@ -829,6 +650,13 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
     mg.G = G;
     mg.S = plan.S;
     mg.c = c;
+    mg.k_cache = (const uint8_t *)p->k_cache;
+    mg.v_cache = (const uint8_t *)p->v_cache;
+    mg.tok_stride = d->kv_token_stride;
+    mg.head_stride = d->kv_head_stride;
+    mg.tail_begin = plan.s0 + plan.n_chunks * kChunk;
+    mg.n_tail = (int32_t)(plan.R - plan.n_chunks * kChunk);
+    mg.kv_type = d->kv_type;
     for (int i = 0; i < TV_MAX_NODES; ++i) mg.anc[i] = 0;
     for (int i = 0; i < n; ++i) {
         uint64_t mk = 0;

@@ -41,7 +41,7 @@ struct SplitPlan {
     RowPlan rows;
     int64_t s0;       // first cache row in the window
     int64_t R;        // cache rows in the window
-    int64_t n_chunks; // ceil(R / kChunk)
+    int64_t n_chunks; // whole chunks of the window: R / kChunk
     int S;            // key-range splits per (KV head, row group)
 };
 

@@ -1,0 +1,266 @@
+// Pieces shared by the split kernels (internal header of libtv.so).
+#pragma once
+
+#include <math.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32;
+
+// Keeps the scheduler from hoisting every LDS fragment load of an unrolled
+// loop to its top, which would need a register per fragment.
+#ifndef TV_NO_FENCE
+#define TV_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define TV_SCHED_FENCE()
+#endif
+
+constexpr float kTau = 8.0f;
+constexpr float kNegBig = -1.0e30f;
+
+struct SplitArgs {
+    const uint8_t *k_cache;
+    const uint8_t *v_cache;
+    int64_t tok_stride;
+    int64_t head_stride;
+    const _Float16 *q;
+    float *ws_o;   // [S][NR][D] unnormalised partial outputs
+    float *ws_ml;  // [S][NR][2] running max (log2 units) and row sum
+    int64_t s0;
+    int64_t key_end;  // end of the rows covered by whole chunks
+    int64_t n_chunks;
+    int32_t NR;  // n * H_q
+    int32_t H_q;
+    int32_t G;
+    int32_t M;  // G * n
+    int32_t S;
+    float c;  // scale * log2(e)
+};
+
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2 as_h2(u32 x) { return __builtin_bit_cast(h2, x); }
+
+// fp32 pair -> fp16 pair (round toward zero), one instruction
+__device__ __forceinline__ h2 pk_rtz(float a, float b)
+{
+    return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// acc + p.x + p.y in fp32 (exact products with 1, fp32 sums)
+__device__ __forceinline__ float add_pair(h2 p, float acc)
+{
+    const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, p), one, acc, false);
+}
+
+// 8 Q4_0 codes packed in one dword (code bytes 4k..4k+3 of a block) -> the
+// exact values code - 8 as four fp16 pairs: [0] = elements (4k, 4k+2),
+// [1] = (4k+1, 4k+3), [2] = (4k+16, 4k+18), [3] = (4k+17, 4k+19).
+// 0x6400 | c is fp16 1024 + c; 0x6400 | (c << 4) is 1024 + 16 c.
+__device__ __forceinline__ void q4_unpack(u32 x, h2 v[4])
+{
+    const u32 y = x >> 8;
+    const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    v[0] = as_h2((x & 0x000F000Fu) | 0x64006400u) - off;
+    v[1] = as_h2((y & 0x000F000Fu) | 0x64006400u) - off;
+    v[2] = __builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+    v[3] = __builtin_elementwise_fma(as_h2((y & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+}
+
+// Position of chunk key kappa (0..63) in a transposed V row: inside each group
+// of 32 keys, the 8 keys a lane group of the PV MFMA consumes are contiguous.
+__device__ __forceinline__ int vpos(int kappa)
+{
+    return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
+}
+
+template <int D, int KVT>
+struct Stage {
+    static constexpr int NB = D / 32;   // 32-wide blocks per row
+    static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
+    static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
+    static constexpr int VSTR = kChunk + 8;  // V^T row stride in LDS (halves)
+    static constexpr int KELEMS = kChunk * KSTR;
+    static constexpr int VELEMS = D * VSTR;
+    static constexpr int ELEMS = KELEMS + VELEMS;
+    // raw registers per thread for the next chunk
+    static constexpr int RAW = KVT == TV_KV_Q4_0 ? NK * 5 : NK * 16;
+};
+
+__device__ __forceinline__ float wave_max_16_32(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+// max over the four lanes {l, l^16, l^32, l^48} with the gfx950 row-swap
+// permutes: each swap hands every lane the value of its partner row, one of
+// the two results being the lane's own value.
+__device__ __forceinline__ float xmax_16_32(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float wave_sum_16_32(float x)
+{
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Rescale one query tile's state when its chunk max mnew exceeds the running
+// max by more than kTau anywhere in the wave.
+template <int NDT>
+__device__ __forceinline__ void maybe_rescale(float mnew, float &m, float &l, f4 (&o)[NDT])
+{
+    const bool need = mnew > m + kTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mm = fmaxf(m, mnew);
+        const float f = __builtin_amdgcn_exp2f(m - mm);
+        l *= f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= f;
+        m = mm;
+    }
+}
+
+struct SplitArgs;
+typedef void (*split_fn)(const SplitArgs);
+
+// Tiles of one row group. Own tile k of wave w is t0 + 4k + w, shared tile u
+// is t0 + 4*NOWN + u; tiles at or past t_end are padding (zero queries,
+// results dropped), so every wave runs the same instructions.
+struct TileMap {
+    int t0, t_end;
+    __device__ __forceinline__ void init(int M, int rg, int RG)
+    {
+        const int T = (M + 15) / 16;
+        const int tb = T / RG, te = T % RG;
+        const int Tg = tb + (rg < te ? 1 : 0);
+        t0 = rg * tb + (rg < te ? rg : te);
+        t_end = t0 + Tg;
+    }
+};
+
+// Q fragments of one tile (B operand of S^T = K Q^T): lane (col, grp) holds
+// query row 16*tile + col, 8 values per 32-wide block. For Q4_0 the 8 values
+// follow the element order of q4_unpack, for F16 the natural order. Zero for
+// padding rows.
+template <int D, int KVT>
+__device__ __forceinline__ void load_q_frags(const SplitArgs &a, int gkv, int tile, int t_end, int col, int grp,
+                                             h8 (&qf)[D / 32])
+{
+    const int r = 16 * tile + col;
+    if (tile < t_end && r < a.M) {
+        const int node = r / a.G, h = gkv * a.G + r % a.G;
+        const _Float16 *qr = a.q + ((int64_t)node * a.H_q + h) * D;
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) {
+            if constexpr (KVT == TV_KV_Q4_0) {
+                const h4 lo = *(const h4 *)(qr + 32 * bb + 4 * grp);
+                const h4 hi = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
+                h8 f;
+                f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
+                f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
+                qf[bb] = f;
+            } else {
+                qf[bb] = *(const h8 *)(qr + 32 * bb + 8 * grp);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) qf[bb] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+}
+
+// Writes the split's partial state (running max in log2 units, row sum,
+// unnormalised output) of every query row. Own tiles go straight to the
+// workspace; the four waves' partial states of a shared tile are combined
+// through LDS (`scratch`, at least scratch_bytes long, free once called).
+template <int D, int NOWN, int NSH>
+__device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scratch, int scratch_bytes, int tid,
+                                               int w, int col, int grp, int gkv, int split, int t_end,
+                                               const int (&tile)[NOWN + NSH], f4 (&o)[NOWN + NSH][D / 16],
+                                               float (&m)[NOWN + NSH], float (&l)[NOWN + NSH])
+{
+    constexpr int NDT = D / 16;
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) {
+        const float lt = wave_sum_16_32(l[k]);
+        const int r = 16 * tile[k] + col;
+        if (tile[k] < t_end && r < a.M) {
+            const int node = r / a.G, h = gkv * a.G + r % a.G;
+            const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
+            float *op = a.ws_o + row * D + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *(f4 *)(op + 16 * dt) = o[k][dt];
+            if (grp == 0) {
+                a.ws_ml[2 * row] = m[k];
+                a.ws_ml[2 * row + 1] = lt;
+            }
+        }
+    }
+    if constexpr (NSH > 0) {
+        __syncthreads();  // every wave is done with the K/V stages
+        float *so = (float *)scratch;            // [NSH][4][16][D]
+        float *sml = so + NSH * 4 * 16 * D;      // [NSH][4][16][2]
+        (void)scratch_bytes;
+#pragma unroll
+        for (int u = 0; u < NSH; ++u) {
+            const float lt = wave_sum_16_32(l[NOWN + u]);
+            float *dst = so + ((u * 4 + w) * 16 + col) * D + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *(f4 *)(dst + 16 * dt) = o[NOWN + u][dt];
+            if (grp == 0) {
+                sml[((u * 4 + w) * 16 + col) * 2] = m[NOWN + u];
+                sml[((u * 4 + w) * 16 + col) * 2 + 1] = lt;
+            }
+        }
+        __syncthreads();
+        for (int u = 0; u < NSH; ++u) {
+            if (tile[NOWN + u] >= t_end) continue;
+            for (int e = tid; e < 16 * D; e += 256) {
+                const int qr = e / D, d = e % D;
+                const int r = 16 * tile[NOWN + u] + qr;
+                if (r >= a.M) continue;
+                float mw[4], mx = kNegBig;
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) {
+                    mw[ww] = sml[((u * 4 + ww) * 16 + qr) * 2];
+                    mx = fmaxf(mx, mw[ww]);
+                }
+                float acc = 0.f, lsum = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) {
+                    const float f = __builtin_amdgcn_exp2f(mw[ww] - mx);
+                    acc += f * so[((u * 4 + ww) * 16 + qr) * D + d];
+                    lsum += f * sml[((u * 4 + ww) * 16 + qr) * 2 + 1];
+                }
+                const int node = r / a.G, h = gkv * a.G + r % a.G;
+                const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
+                a.ws_o[row * D + d] = acc;
+                if (d == 0) {
+                    a.ws_ml[2 * row] = mx;
+                    a.ws_ml[2 * row + 1] = lsum;
+                }
+            }
+        }
+    }
+}
+
+split_fn pick_split_q4(int D, int nown, int nsh);
+
+}  // namespace tv

@@ -1,0 +1,472 @@
+// Split kernel for Q4_0 caches, software-pipelined for gfx950.
+//
+// Same decomposition as the generic split kernel (one workgroup of four
+// wave64s per key-range split, KV head and row group; the packed
+// GQA-group x tree-node query rows cut into 16-row MFMA tiles, own and
+// shared), but the dequantisation of chunk c+1 is interleaved with the MFMAs
+// of chunk c so that the VALU work runs in the shadow of the matrix cores:
+//
+//   iteration c:  barrier
+//                 S^T(c) = K Q^T MFMAs   + dequantise K(c+1) into the other
+//                                          LDS stage, one code dword per block
+//                 load raw K(c+2)
+//                 online softmax(c)
+//                 O^T += V^T P^T MFMAs   + dequantise V(c+1)
+//                 load raw V(c+2)
+//
+// Raw Q4_0 bytes travel HBM -> registers one iteration ahead. LDS stores are
+// laid out so that the writes of a wave hit distinct banks: K rows are
+// written one key per lane, transposed V rows four keys (8 bytes) per lane
+// with the key groups fastest across lanes.
+//
+// Method: DDTree tree verify over a Q4_0 KV cache ("Luce DFlash: 単一RTX 3090
+// で最大2倍のスループットを目指すQwen3.6-27B", feature list; "We got 207 tok/s
+// with Qwen3.5-27B on an RTX 3090", "What we built vs what we didn't").
+
+#include "tv_split_common.h"
+
+namespace tv {
+
+// Per-thread share of one 64-key chunk.
+//   K: key (tid & 63), half-blocks [u*HB, (u+1)*HB) with u = tid >> 6; one
+//      half-block is 16 values (8 code bytes) of one 32-value block.
+//   V: NKV consecutive keys starting at NKV * (tid % KG), one half-block
+//      (block b, half h) of each.
+template <int D>
+struct Q4Share {
+    static constexpr int NB = D / 32;
+    static constexpr int HB = NB / 2;    // K half-blocks per thread
+    static constexpr int NKV = NB / 2;   // V keys per thread
+    static constexpr int KG = 64 / NKV;  // V key groups
+    static constexpr int RAWK = 4 * HB;  // per half-block: scale dword + 3-dword code window
+    static constexpr int RAWV = 4 * NKV;
+};
+
+__device__ __forceinline__ u32 and_or(u32 x, u32 m, u32 o)
+{
+    u32 r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+    return r;
+}
+
+// code dword (8 codes) -> the exact values code - 8 in four fp16 pairs, same
+// element order as q4_unpack.
+__device__ __forceinline__ void q4_unpack_ao(u32 x, u32 magic, h2 v[4])
+{
+    const u32 y = x >> 8;
+    const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    v[0] = as_h2(and_or(x, 0x000F000Fu, magic)) - off;
+    v[1] = as_h2(and_or(y, 0x000F000Fu, magic)) - off;
+    v[2] = __builtin_elementwise_fma(as_h2(and_or(x, 0x00F000F0u, magic)), sixteenth, off_hi);
+    v[3] = __builtin_elementwise_fma(as_h2(and_or(y, 0x00F000F0u, magic)), sixteenth, off_hi);
+}
+
+// Byte offset, inside a row, of the dword holding the scale of block b and
+// of the 3-dword window holding the 8 code bytes of half h; the codes start
+// 2 + 2*(b & 1) bytes into the window. Every window lies inside its row.
+__device__ __forceinline__ int scale_dword_off(int b) { return 18 * b - 2 * (b & 1); }
+__device__ __forceinline__ int window_off(int b, int h) { return 18 * b + 8 * h - 2 * (b & 1); }
+
+__device__ __forceinline__ void load_half_block(const uint8_t *row, int b, int h, u32 *r)
+{
+    r[0] = *(const u32 *)(row + scale_dword_off(b));
+    const u32 *wp = (const u32 *)(row + window_off(b, h));
+    r[1] = wp[0];
+    r[2] = wp[1];
+    r[3] = wp[2];
+}
+
+// scale (fp16 bits) and the two code dwords of a loaded half-block
+__device__ __forceinline__ void split_half_block(const u32 *r, int b, _Float16 &s, u32 &c0, u32 &c1)
+{
+    const bool odd = b & 1;
+    s = __builtin_bit_cast(_Float16, (uint16_t)(odd ? (r[0] >> 16) : (r[0] & 0xFFFFu)));
+    c0 = odd ? r[2] : __builtin_amdgcn_alignbyte(r[2], r[1], 2);
+    c1 = odd ? r[3] : __builtin_amdgcn_alignbyte(r[3], r[2], 2);
+}
+
+template <int D>
+struct Q4Loader {
+    using Sh = Q4Share<D>;
+    static constexpr int NB = Sh::NB;
+    const uint8_t *kbase;  // K cache of this KV head
+    const uint8_t *vbase;
+    int64_t tok_stride;
+    int kk, u;         // K: key in chunk, half-block group
+    int kg, vb, vh;    // V: key group, block, half
+    u32 krow, vrow;    // byte offsets of this thread's first K / V row inside a chunk
+    u32 rk[Sh::RAWK];
+    u32 rv[Sh::RAWV];
+
+    __device__ __forceinline__ void init(const SplitArgs &a, int gkv, int tid)
+    {
+        kbase = a.k_cache + (int64_t)gkv * a.head_stride;
+        vbase = a.v_cache + (int64_t)gkv * a.head_stride;
+        tok_stride = a.tok_stride;
+        kk = tid & 63;
+        u = tid >> 6;
+        kg = tid % Sh::KG;
+        const int rest = tid / Sh::KG;
+        vb = rest % NB;
+        vh = rest / NB;
+        krow = (u32)(kk * tok_stride);
+        vrow = (u32)(Sh::NKV * kg * tok_stride);
+    }
+
+    // Every key of a chunk is a committed row (the tail of the window that
+    // does not fill a chunk is left to the merge kernel), so no bounds checks.
+    // The chunk base is uniform; per-thread offsets are 32-bit.
+    __device__ __forceinline__ void load_k(int64_t chunk_row)
+    {
+        const uint8_t *cb = kbase + chunk_row * tok_stride;
+#pragma unroll
+        for (int t = 0; t < Sh::HB; ++t) {
+            const int j = u * Sh::HB + t;
+            load_half_block(cb + krow, j >> 1, j & 1, rk + 4 * t);
+        }
+    }
+
+    __device__ __forceinline__ void load_v(int64_t chunk_row)
+    {
+        const uint8_t *cb = vbase + chunk_row * tok_stride;
+#pragma unroll
+        for (int q = 0; q < Sh::NKV; ++q) load_half_block(cb + vrow + (u32)(q * tok_stride), vb, vh, rv + 4 * q);
+    }
+
+    // K piece j (0..NB-1): code dword j of this thread -> one 16-byte store
+    __device__ __forceinline__ void k_piece(int j, _Float16 *ks, u32 magic) const
+    {
+        const int t = j >> 1, k = j & 1;
+        const int hbi = u * Sh::HB + t, b = hbi >> 1, h = hbi & 1;
+        _Float16 s;
+        u32 c0, c1;
+        split_half_block(rk + 4 * t, b, s, c0, c1);
+        h2 v[4];
+        q4_unpack_ao(k ? c1 : c0, magic, v);
+        const h2 s2 = {s, s};
+        h8 o;
+        o.s01 = v[0] * s2;
+        o.s23 = v[1] * s2;
+        o.s45 = v[2] * s2;
+        o.s67 = v[3] * s2;
+        // code dword index inside the block is 2h + k
+        *(h8 *)(ks + kk * Stage<D, TV_KV_Q4_0>::KSTR + 32 * b + 8 * (2 * h + k)) = o;
+    }
+
+    static constexpr int V_PIECES = Sh::NKV >= 2 ? 4 : 2;
+
+    // V piece p: for NKV >= 2, code dword k = p >> 1 and element half
+    // (p & 1 ? the "b" bytes : the "a" bytes) of all NKV keys
+    __device__ __forceinline__ void v_piece(int p, _Float16 *vt, u32 magic) const
+    {
+        constexpr int VSTR = Stage<D, TV_KV_Q4_0>::VSTR;
+        const int pos = vpos(Sh::NKV * kg);
+        if constexpr (Sh::NKV >= 2) {
+            const int k = p >> 1;
+            const bool second = p & 1;
+            const int e0 = 8 * vh + 4 * k;
+            h2 vals[Sh::NKV / 2][4];
+#pragma unroll
+            for (int pr = 0; pr < Sh::NKV / 2; ++pr) {
+                _Float16 s0, s1;
+                u32 a0, a1, b0, b1;
+                split_half_block(rv + 4 * (2 * pr), vb, s0, a0, a1);
+                split_half_block(rv + 4 * (2 * pr + 1), vb, s1, b0, b1);
+                const u32 x0 = k ? a1 : a0, x1 = k ? b1 : b0;
+                const u32 z = __builtin_amdgcn_perm(x1, x0, second ? 0x07060302u : 0x05040100u);
+                q4_unpack_ao(z, magic, vals[pr]);
+                const h2 s2 = {s0, s1};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) vals[pr][t] = vals[pr][t] * s2;
+            }
+            // element of vals[*][t]: a-bytes give e0, e0+1, e0+16, e0+17;
+            // b-bytes give e0+2, e0+3, e0+18, e0+19
+            const int base_e = e0 + (second ? 2 : 0);
+            const int ev[4] = {base_e, base_e + 1, base_e + 16, base_e + 17};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                _Float16 *dst = vt + (32 * vb + ev[t]) * VSTR + pos;
+                if constexpr (Sh::NKV == 4) {
+                    h4 w4;
+                    w4.s01 = vals[0][t];
+                    w4.s23 = vals[1][t];
+                    *(h4 *)dst = w4;
+                } else {
+                    *(h2 *)dst = vals[0][t];
+                }
+            }
+        } else {
+            // one key: code dword p of the half-block, fp16 stores
+            _Float16 s;
+            u32 c0, c1;
+            split_half_block(rv, vb, s, c0, c1);
+            h2 v[4];
+            q4_unpack_ao(p ? c1 : c0, magic, v);
+            const h2 s2 = {s, s};
+            const int e0 = 8 * vh + 4 * p;
+            const int ev[8] = {e0, e0 + 2, e0 + 1, e0 + 3, e0 + 16, e0 + 18, e0 + 17, e0 + 19};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const h2 w = v[t] * s2;
+                vt[(32 * vb + ev[2 * t]) * VSTR + pos] = w.x;
+                vt[(32 * vb + ev[2 * t + 1]) * VSTR + pos] = w.y;
+            }
+        }
+    }
+};
+
+// Split kernel. Own tiles: each wave holds NOWN query tiles for all D.
+// Shared tiles (the one or two tiles left over when the tile count is not a
+// multiple of four): every wave computes their scores and softmax over the
+// whole chunk (identical in the four waves) but accumulates only its quarter
+// of D, so a shared tile costs a quarter of an own tile's registers. Each
+// wave walks the D-tiles rotated by its index, so that its shared quarter is
+// the first NDT/4 positions of every k-step and every index into the
+// register arrays stays a compile-time constant.
+template <int D, int NOWN, int NSH>
+__global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
+{
+    using St = Stage<D, TV_KV_Q4_0>;
+    using L = Q4Loader<D>;
+    constexpr int NB = St::NB;
+    constexpr int NDT = D / 16;
+    constexpr int NDQ = NDT / 4;  // D-tiles of a shared tile per wave
+    constexpr int NS = NOWN + NSH;
+    static_assert(NS >= 1 && NS <= kMaxSlots, "slots");
+    __shared__ __attribute__((aligned(16))) _Float16 lds[2 * St::ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x, gkv = blockIdx.y, rg = blockIdx.z;
+
+    TileMap tm;
+    tm.init(a.M, rg, gridDim.z);
+    int tile[NS];
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) tile[k] = tm.t0 + 4 * k + w;
+#pragma unroll
+    for (int u = 0; u < NSH; ++u) tile[NOWN + u] = tm.t0 + 4 * NOWN + u;
+
+    h8 qf[NS][NB];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) load_q_frags<D, TV_KV_Q4_0>(a, gkv, tile[k], tm.t_end, col, grp, qf[k]);
+    // Q fragments are read only as MFMA B operands, which may live in AGPRs;
+    // parking them there leaves the VGPRs to the accumulators and the pipeline.
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) asm volatile("" : "+a"(qf[k][bb]));
+
+    f4 o[NOWN > 0 ? NOWN : 1][NDT];
+    f4 osh[NSH > 0 ? NSH : 1][NDQ];
+    float m[NS], l[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        m[k] = kNegBig;
+        l[k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k)
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) o[k][j] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NSH; ++u)
+#pragma unroll
+        for (int j = 0; j < NDQ; ++j) osh[u][j] = (f4){0.f, 0.f, 0.f, 0.f};
+
+    const int64_t c_begin = a.n_chunks * split / a.S;
+    const int64_t c_end = a.n_chunks * (split + 1) / a.S;
+    const u32 magic = 0x64006400u;
+    const int rot = NDQ * w;  // D-tile at loop position j is (j + rot) % NDT
+
+    L ld;
+    ld.init(a, gkv, tid);
+    // prologue: chunk c_begin dequantised into stage 0, raw bytes of the next
+    ld.load_k(a.s0 + c_begin * kChunk);
+    ld.load_v(a.s0 + c_begin * kChunk);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) ld.k_piece(j, lds, magic);
+#pragma unroll
+    for (int p = 0; p < L::V_PIECES; ++p) ld.v_piece(p, lds + St::KELEMS, magic);
+    if (c_begin + 1 < c_end) {
+        ld.load_k(a.s0 + (c_begin + 1) * kChunk);
+        ld.load_v(a.s0 + (c_begin + 1) * kChunk);
+    }
+
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int st = (int)((c - c_begin) & 1);
+        const _Float16 *ks = lds + st * St::ELEMS;
+        const _Float16 *vt = ks + St::KELEMS;
+        _Float16 *ks_n = lds + (st ^ 1) * St::ELEMS;
+        _Float16 *vt_n = ks_n + St::KELEMS;
+        __syncthreads();
+
+        // ---- S^T = K Q^T for every slot and the 4 key tiles of the chunk,
+        // with the K dequantisation of chunk c+1 in between. K fragments
+        // stream through a 3-entry ring, two ahead of use.
+        constexpr int TOT = NB * 4;
+        f4 sacc[NS][4];
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sacc[k][kt] = (f4){0.f, 0.f, 0.f, 0.f};
+        auto kfrag = [&](int i) -> h8 {
+            const int bb = i / 4, kt = i % 4;
+            return *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
+        };
+        h8 kr[3];
+        kr[0] = kfrag(0);
+        kr[1] = kfrag(1);
+#pragma unroll
+        for (int i = 0; i < TOT; ++i) {
+            if (i + 2 < TOT) kr[(i + 2) % 3] = kfrag(i + 2);
+            const int bb = i / 4, kt = i % 4;
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[i % 3], qf[k][bb], sacc[k][kt], 0, 0, 0);
+            if (kt == 3) {
+                ld.k_piece(bb, ks_n, magic);
+                TV_SCHED_FENCE();
+            }
+        }
+        if (c + 2 < c_end) ld.load_k(a.s0 + (c + 2) * kChunk);
+
+        // ---- running maxima (trees: the VALU's dependent-issue latency is
+        // long), one wave-uniform branch for the rare rescale of all slots
+        float mnew[NS];
+        bool need = false;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            float t[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                t[kt] = fmaxf(fmaxf(sacc[k][kt][0], sacc[k][kt][1]), fmaxf(sacc[k][kt][2], sacc[k][kt][3]));
+            mnew[k] = xmax_16_32(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]))) * a.c;
+            need = need || (mnew[k] > m[k] + kTau);
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const float mm = fmaxf(m[k], mnew[k]);
+                const float f = __builtin_amdgcn_exp2f(m[k] - mm);
+                l[k] *= f;
+                m[k] = mm;
+                if (k < NOWN) {
+#pragma unroll
+                    for (int j = 0; j < NDT; ++j) o[k < NOWN ? k : 0][j] *= f;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NDQ; ++j) osh[k >= NOWN ? k - NOWN : 0][j] *= f;
+                }
+            }
+        }
+
+        // ---- fp16 P^T fragments; k-step kk covers key tiles 2kk, 2kk+1
+        h8 pf[NS][2];
+        auto make_p = [&](int k, int kk) {
+            h2 p[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int kt = 2 * kk + (t >> 1), i0 = 2 * (t & 1);
+                p[t] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k][kt][i0], a.c, -m[k])),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k][kt][i0 + 1], a.c, -m[k])));
+            }
+            l[k] += add_pair(p[0], add_pair(p[1], 0.f)) + add_pair(p[2], add_pair(p[3], 0.f));
+            h8 fr;
+            fr.s01 = p[0];
+            fr.s23 = p[1];
+            fr.s45 = p[2];
+            fr.s67 = p[3];
+            pf[k][kk] = fr;
+        };
+#pragma unroll
+        for (int k = 0; k < NS; ++k) make_p(k, 0);
+
+        // ---- O^T += V^T P^T. k-step 0 runs while the P of k-step 1 is
+        // computed; k-step 1 runs while V(c+1) is dequantised.
+        constexpr int TV = 2 * NDT;
+        auto vfrag = [&](int i) -> h8 {
+            const int kk = i / NDT, j = i % NDT;
+            const int dt = (j + rot) & (NDT - 1);
+            return *(const h8 *)(vt + (16 * dt + col) * St::VSTR + 32 * kk + 8 * grp);
+        };
+        constexpr int VP = L::V_PIECES;
+        constexpr int VSTEP = NDT / VP;
+        h8 vr[3];
+        vr[0] = vfrag(0);
+        vr[1] = vfrag(1);
+#pragma unroll
+        for (int i = 0; i < TV; ++i) {
+            if (i + 2 < TV) vr[(i + 2) % 3] = vfrag(i + 2);
+            const int kk = i / NDT, j = i % NDT;
+#pragma unroll
+            for (int k = 0; k < NOWN; ++k)
+                o[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 3], pf[k][kk], o[k][j], 0, 0, 0);
+            if (j < NDQ) {
+#pragma unroll
+                for (int u = 0; u < NSH; ++u)
+                    osh[u][j < NDQ ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 3], pf[NOWN + u][kk],
+                                                                                   osh[u][j < NDQ ? j : 0], 0, 0, 0);
+            }
+            if (i == 1) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) make_p(k, 1);
+            }
+            if (kk == 1 && (j + 1) % VSTEP == 0) {
+                ld.v_piece((j + 1) / VSTEP - 1, vt_n, magic);
+                TV_SCHED_FENCE();
+            }
+        }
+        if (c + 2 < c_end) ld.load_v(a.s0 + (c + 2) * kChunk);
+    }
+
+    // ---- partial states: own tiles by every wave; shared tiles by every
+    // wave for its quarter of D (their row maxima and sums are identical in
+    // all waves and written by wave 0)
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const float lt = wave_sum_16_32(l[k]);
+        const int r = 16 * tile[k] + col;
+        if (tile[k] < tm.t_end && r < a.M) {
+            const int node = r / a.G, h = gkv * a.G + r % a.G;
+            const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
+            float *op = a.ws_o + row * D + 4 * grp;
+            if (k < NOWN) {
+#pragma unroll
+                for (int j = 0; j < NDT; ++j) *(f4 *)(op + 16 * ((j + rot) & (NDT - 1))) = o[k < NOWN ? k : 0][j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < NDQ; ++j) *(f4 *)(op + 16 * (j + rot)) = osh[k >= NOWN ? k - NOWN : 0][j];
+            }
+            if (grp == 0 && (k < NOWN || w == 0)) {
+                a.ws_ml[2 * row] = m[k];
+                a.ws_ml[2 * row + 1] = lt;
+            }
+        }
+    }
+}
+
+template <int D>
+static split_fn pick_q4(int nown, int nsh)
+{
+#define TV_CASE(O, S) \
+    if (nown == O && nsh == S) return split_q4_kernel<D, O, S>;
+    TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
+    TV_CASE(3, 0)
+#undef TV_CASE
+    return nullptr;
+}
+
+split_fn pick_split_q4(int D, int nown, int nsh)
+{
+    if (D == 64) return pick_q4<64>(nown, nsh);
+    if (D == 128) return pick_q4<128>(nown, nsh);
+    if (D == 256) return pick_q4<256>(nown, nsh);
+    return nullptr;
+}
+
+}  // namespace tv
