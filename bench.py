@@ -46,6 +46,42 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_128k_q4_0_hbm_traffic.md")
+
+
+def kernel_sources_sha256():
+    """Hash of the HIP sources and build flags of libtv.so: a stored counter
+    figure applies only to the kernels it was measured on."""
+    import hashlib
+    pkg = os.path.join(ROOT, "tree_verify_attention_ddtree_amd")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(pkg, "csrc"))):
+        with open(os.path.join(pkg, "csrc", name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes (copy-calibrated) stored under profiles/, or None when
+    the kernels have changed since they were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("sources_sha256") != kernel_sources_sha256():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_calibration(nbytes, steps):
     """A plain device-to-device copy of known size, the yardstick that scales
     the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
@@ -155,6 +191,7 @@ def main():
     tflops = flops / (ms_attn * 1e-3) / 1e12
     chain_kv_gbps = kv_bytes / (ms_chain * 1e-3) / 1e9
 
+    traffic = measured_traffic() if (args.workload == "long" and args.kv == "q4_0") else None
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_step,
@@ -188,7 +225,8 @@ def main():
             "peak": MFMA_FP16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per attention launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
             "algorithmic_flops": flops,
             "algorithmic_kv_bytes": kv_bytes,
         },
