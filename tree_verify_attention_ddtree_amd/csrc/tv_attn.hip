@@ -455,18 +455,28 @@ __device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, in
     }
 }
 
-// One workgroup per output row. Thread t owns the 4 output values of d-quad
-// t % (D/4) for the splits s = t / (D/4) (mod D-quad groups); the groups are
-// summed through LDS at the end. Wave 0 scores the tree ancestors first.
+// One workgroup of 256 threads per output row (node i, query head h), in
+// three rounds of independent loads:
+//   1. thread (split group sg, d-quad dq) loads the partial states of its
+//      splits s = sg, sg + NGR, ... and folds them against their own maximum;
+//      at the same time the threads score the row's extra keys (its tree
+//      ancestors, then the window's tail rows), KL lanes per key;
+//   2. the maximum over splits and extra keys;
+//   3. the extra keys' V rows are spread over the split groups; the groups'
+//      sums meet in LDS.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 {
     constexpr int QD = D / 4;       // d-quads per row
     constexpr int NGR = 256 / QD;   // split groups
-    constexpr int PL = D / 64;      // values per lane for the tree dot products
-    __shared__ float sc[TV_MAX_NODES];
-    __shared__ float stl[kChunk];
-    __shared__ float red[256];
+    constexpr int KL = 16;          // lanes per extra key
+    constexpr int KPT = D / KL;     // values per lane of a key's dot product
+    constexpr int KPASS = 256 / KL; // extra keys per pass
+    constexpr int SMAX = 8;         // splits per thread held in registers
+    static_assert(32 % KPT == 0, "a lane's key slice lies inside one 32-value block");
+    __shared__ float sk[TV_MAX_NODES + kChunk];
+    __shared__ float red_s[NGR];
+    __shared__ float red_k[4];
     __shared__ __attribute__((aligned(16))) float acc_s[NGR][D];
     __shared__ float l_s[NGR];
 
@@ -474,91 +484,116 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     const int row = blockIdx.x;
     const int i = row / a.H_q, h = row % a.H_q, g = h / a.G;
     const uint64_t anc = a.anc[i];
-
-    // tree scores (wave 0), kept in LDS
-    float mt = -INFINITY;
-    if (w == 0) {
-        float qv[PL];
-#pragma unroll
-        for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
-        for (uint64_t mm = anc; mm; mm &= mm - 1) {
-            const int j = __builtin_ctzll(mm);
-            const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + lane * PL;
-            float part = 0.f;
-#pragma unroll
-            for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], (float)kr[p], part);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-            const float sj = part * a.c;
-            if (lane == 0) sc[j] = sj;
-            mt = fmaxf(mt, sj);
-        }
-    }
-    // tail cache rows (wave 1)
+    const int na = __builtin_popcountll(anc);
+    const int nk = na + a.n_tail;
     const uint8_t *kh = a.k_cache + (int64_t)g * a.head_stride;
     const uint8_t *vh = a.v_cache + (int64_t)g * a.head_stride;
-    if (w == 1 && a.n_tail > 0) {
-        float qv[PL];
-#pragma unroll
-        for (int p = 0; p < PL; ++p) qv[p] = (float)a.q[(int64_t)row * D + lane * PL + p];
-        for (int j = 0; j < a.n_tail; ++j) {
-            float kv[PL];
-            cache_values<PL>(kh + (a.tail_begin + j) * a.tok_stride, a.kv_type, lane * PL, kv);
-            float part = 0.f;
-#pragma unroll
-            for (int p = 0; p < PL; ++p) part = __builtin_fmaf(qv[p], kv[p], part);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-            const float sj = part * a.c;
-            if (lane == 0) stl[j] = sj;
-            mt = fmaxf(mt, sj);
-        }
-    }
-    // max over the split maxima, the tree and the tail
-    float mx = (w == 0 || w == 1) ? mt : -INFINITY;
-    for (int s = t; s < a.S; s += 256) mx = fmaxf(mx, a.ws_ml[((int64_t)s * a.NR + row) * 2]);
-    red[t] = mx;
-    __syncthreads();
-    for (int k = 128; k >= 1; k >>= 1) {
-        if (t < k) red[t] = fmaxf(red[t], red[t + k]);
-        __syncthreads();
-    }
-    const float mstar = red[0];
 
+    // ---- round 1a: this thread's splits, folded against their maximum
     const int dq = t % QD, sg = t / QD;
+    float ms = kNegBig;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
-#pragma unroll 4
-    for (int s = sg; s < a.S; s += NGR) {
-        const int64_t base = (int64_t)s * a.NR + row;
-        const float f = exp2f(a.ws_ml[2 * base] - mstar);
-        L = __builtin_fmaf(f, a.ws_ml[2 * base + 1], L);
-        const f4 o = *(const f4 *)(a.ws_o + base * D + 4 * dq);
-        acc += f * o;
+    {
+        float mv[SMAX], lv[SMAX];
+        f4 ov[SMAX];
+        for (int s0 = sg; s0 < a.S; s0 += NGR * SMAX) {
+#pragma unroll
+            for (int k = 0; k < SMAX; ++k) {
+                const int s = s0 + NGR * k;
+                if (s < a.S) {
+                    const int64_t base = (int64_t)s * a.NR + row;
+                    mv[k] = a.ws_ml[2 * base];
+                    lv[k] = a.ws_ml[2 * base + 1];
+                    ov[k] = *(const f4 *)(a.ws_o + base * D + 4 * dq);
+                } else {
+                    mv[k] = kNegBig;
+                    lv[k] = 0.f;
+                    ov[k] = (f4){0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            float mb = ms;
+#pragma unroll
+            for (int k = 0; k < SMAX; ++k) mb = fmaxf(mb, mv[k]);
+            const float r = exp2f(ms - mb);
+            acc *= r;
+            L *= r;
+#pragma unroll
+            for (int k = 0; k < SMAX; ++k) {
+                const float f = exp2f(mv[k] - mb);
+                L = __builtin_fmaf(f, lv[k], L);
+                acc += f * ov[k];
+            }
+            ms = mb;
+        }
     }
-    if (sg == 0) {
-        for (uint64_t mm = anc; mm; mm &= mm - 1) {
+    // ---- round 1b: scores of the extra keys (ancestors, then tail rows)
+    float mk = -INFINITY;
+    {
+        const int kl = t % KL;
+        float qv[KPT];
+#pragma unroll
+        for (int p = 0; p < KPT; ++p) qv[p] = (float)a.q[(int64_t)row * D + kl * KPT + p];
+        for (int base = 0; base < nk; base += KPASS) {
+            const int kk = base + t / KL;
+            float part = 0.f;
+            if (kk < nk) {
+                float kv[KPT];
+                if (kk < na) {
+                    uint64_t mm = anc;
+                    for (int r = 0; r < kk; ++r) mm &= mm - 1;
+                    const int j = __builtin_ctzll(mm);
+                    const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + kl * KPT;
+#pragma unroll
+                    for (int p = 0; p < KPT; ++p) kv[p] = (float)kr[p];
+                } else {
+                    cache_values<KPT>(kh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, kl * KPT, kv);
+                }
+#pragma unroll
+                for (int p = 0; p < KPT; ++p) part = __builtin_fmaf(qv[p], kv[p], part);
+            }
+#pragma unroll
+            for (int off = KL / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+            if (kk < nk) {
+                const float sj = part * a.c;
+                if (kl == 0) sk[kk] = sj;
+                mk = fmaxf(mk, sj);
+            }
+        }
+    }
+    // ---- round 2: maxima
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off));
+    if (lane == 0) red_k[w] = mk;
+    if (dq == 0) red_s[sg] = ms;
+    __syncthreads();
+    float mstar = fmaxf(fmaxf(red_k[0], red_k[1]), fmaxf(red_k[2], red_k[3]));
+#pragma unroll
+    for (int k = 0; k < NGR; ++k) mstar = fmaxf(mstar, red_s[k]);
+    {
+        const float r = exp2f(ms - mstar);
+        acc *= r;
+        L *= r;
+    }
+    // ---- round 3: the extra keys' V rows, spread over the split groups
+    for (int kk = sg; kk < nk; kk += NGR) {
+        const float f = exp2f(sk[kk] - mstar);
+        L += f;
+        float vv[4];
+        if (kk < na) {
+            uint64_t mm = anc;
+            for (int r = 0; r < kk; ++r) mm &= mm - 1;
             const int j = __builtin_ctzll(mm);
-            const float f = exp2f(sc[j] - mstar);
-            L += f;
             const _Float16 *vr = a.v_tree + ((int64_t)j * a.H_kv + g) * D + 4 * dq;
-            acc.x = __builtin_fmaf(f, (float)vr[0], acc.x);
-            acc.y = __builtin_fmaf(f, (float)vr[1], acc.y);
-            acc.z = __builtin_fmaf(f, (float)vr[2], acc.z);
-            acc.w = __builtin_fmaf(f, (float)vr[3], acc.w);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) vv[p] = (float)vr[p];
+        } else {
+            cache_values<4>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 4 * dq, vv);
         }
-    }
-    if (sg == 1) {
-        for (int j = 0; j < a.n_tail; ++j) {
-            const float f = exp2f(stl[j] - mstar);
-            L += f;
-            float vv[4];
-            cache_values<4>(vh + (a.tail_begin + j) * a.tok_stride, a.kv_type, 4 * dq, vv);
-            acc.x = __builtin_fmaf(f, vv[0], acc.x);
-            acc.y = __builtin_fmaf(f, vv[1], acc.y);
-            acc.z = __builtin_fmaf(f, vv[2], acc.z);
-            acc.w = __builtin_fmaf(f, vv[3], acc.w);
-        }
+        acc.x = __builtin_fmaf(f, vv[0], acc.x);
+        acc.y = __builtin_fmaf(f, vv[1], acc.y);
+        acc.z = __builtin_fmaf(f, vv[2], acc.z);
+        acc.w = __builtin_fmaf(f, vv[3], acc.w);
     }
     *(f4 *)&acc_s[sg][4 * dq] = acc;
     if (dq == 0) l_s[sg] = L;
