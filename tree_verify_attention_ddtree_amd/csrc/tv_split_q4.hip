@@ -182,12 +182,15 @@ struct Q4Loader {
                 for (int t = 0; t < 4; ++t) vals[pr][t] = vals[pr][t] * s2;
             }
             // element of vals[*][t]: a-bytes give e0, e0+1, e0+16, e0+17;
-            // b-bytes give e0+2, e0+3, e0+18, e0+19
-            const int base_e = e0 + (second ? 2 : 0);
-            const int ev[4] = {base_e, base_e + 1, base_e + 16, base_e + 17};
+            // b-bytes give e0+2, e0+3, e0+18, e0+19. One per-thread base
+            // (block, half, key position), the rest immediate offsets.
+            _Float16 *vrow = vt + (32 * vb + 8 * vh) * VSTR + pos;
+            const int de = 4 * k + (second ? 2 : 0);
+            const int ev[4] = {de, de + 1, de + 16, de + 17};
+            (void)e0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                _Float16 *dst = vt + (32 * vb + ev[t]) * VSTR + pos;
+                _Float16 *dst = vrow + ev[t] * VSTR;
                 if constexpr (Sh::NKV == 4) {
                     h4 w4;
                     w4.s01 = vals[0][t];
@@ -389,10 +392,15 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         // ---- O^T += V^T P^T. k-step 0 runs while the P of k-step 1 is
         // computed; k-step 1 runs while V(c+1) is dequantised.
         constexpr int TV = 2 * NDT;
+        // position j reads D-tile (j + rot) % NDT: from vA below the wrap,
+        // from vB = vA - NDT tiles after it, both at the immediate offset of
+        // position j
+        const _Float16 *vA = vt + (16 * rot + col) * St::VSTR + 8 * grp;
+        const _Float16 *vB = vA - NDT * 16 * St::VSTR;
         auto vfrag = [&](int i) -> h8 {
             const int kk = i / NDT, j = i % NDT;
-            const int dt = (j + rot) & (NDT - 1);
-            return *(const h8 *)(vt + (16 * dt + col) * St::VSTR + 32 * kk + 8 * grp);
+            const _Float16 *base = j < NDT - rot ? vA : vB;
+            return *(const h8 *)(base + j * 16 * St::VSTR + 32 * kk);
         };
         constexpr int VP = L::V_PIECES;
         constexpr int VSTEP = NDT / VP;
