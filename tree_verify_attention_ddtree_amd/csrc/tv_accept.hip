@@ -119,15 +119,15 @@ __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
 
     int am = 0;
     if (live) {
-        // the slice maxima of row `lane`, loaded eight at a time
+        // the slice maxima of row `lane`, loaded 32 at a time
         uint64_t b = 0;
         const uint64_t *pr = a.part + (int64_t)lane * a.n_slices;
-        for (int s0 = 0; s0 < a.n_slices; s0 += 8) {
-            uint64_t v[8];
+        for (int s0 = 0; s0 < a.n_slices; s0 += 32) {
+            uint64_t v[32];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = s0 + k < a.n_slices ? pr[s0 + k] : 0ull;
+            for (int k = 0; k < 32; ++k) v[k] = s0 + k < a.n_slices ? pr[s0 + k] : 0ull;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) b = umax64(b, v[k]);
+            for (int k = 0; k < 32; ++k) b = umax64(b, v[k]);
         }
         am = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFu));
         a.argmax_out[lane] = am;
