@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9, help="KV bytes the copies span at least")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=552, help="oracle output rows timed for the CPU baseline")
+    ap.add_argument("--no-full-step", action="store_true", help="skip the 16-layer verify-step measurement")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only copy a device buffer of this many bytes --steps times (HBM counter calibration)")
     return ap.parse_args()
@@ -232,9 +233,79 @@ def main():
         },
     }
 
+    if not args.no_full_step and args.workload == "long" and args.kv == "q4_0":
+        line.update(full_step(tv, synth, dev, stream, max(5, args.steps // 2)))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, logits, parent, tokens, args.cpu_rows)
     print(json.dumps(line), flush=True)
+
+
+def full_step(tv, synth, dev, stream, steps):
+    """A whole verify step of a 16-layer model of the same head layout at
+    32K context: 16 tree-verify attention launches over 16 distinct Q4_0
+    layer caches (604 MB together), then the acceptance. Timed back to back
+    (pipelined) and with the step's result copied to the host and the stream
+    synchronised after every step, as a decode loop must."""
+    import torch
+    w = dict(synth.WORKLOADS["full"])
+    layers = []
+    for layer in range(w["n_layers"]):
+        inp = synth.attn_inputs(**dict(w, seed=5000 + 100 * layer))
+        t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("k_cache", "v_cache", "q", "k_tree", "v_tree")}
+        ts, hs = tv.cache_strides(t["k_cache"], tv.TV_KV_Q4_0)
+        desc, par = tv.make_desc(inp["parent"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"], tv.TV_KV_Q4_0,
+                                 w["n_ctx"], 0, inp["scale"], ts, hs)
+        wsb = tv.tv_attn_workspace_bytes(desc)
+        t["ws"] = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        t["wsb"], t["desc"], t["par"] = wsb, desc, par
+        t["out"] = torch.empty((len(inp["parent"]), w["n_q_heads"], w["head_dim"]), dtype=torch.float32, device=dev)
+        layers.append(t)
+    parent = synth.attn_inputs(**dict(w, seed=5000))["parent"]
+    s = synth.streams(w["seed"])
+    tokens = synth.sibling_distinct_tokens(s["tokens"], parent, w["vocab"])
+    logits, planted_L, _ = synth.planted_logits(s["logits"], parent, tokens, w["vocab"])
+    n = len(parent)
+    lg = torch.from_numpy(logits).to(dev)
+    am = torch.empty(n, dtype=torch.int32, device=dev)
+    res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
+    aws = torch.empty(tv.tv_accept_workspace_bytes(n, w["vocab"]), dtype=torch.uint8, device=dev)
+    host = torch.empty(2 + 2 * n, dtype=torch.int32, pin_memory=True)
+
+    def one_step():
+        for t in layers:
+            tv.tree_verify_attn(t["desc"], t["k_cache"], t["v_cache"], t["q"], t["k_tree"], t["v_tree"], t["out"],
+                                t["ws"], t["wsb"], stream)
+        tv.tree_accept(lg, parent, tokens, am, res, aws, stream)
+
+    for _ in range(3):
+        one_step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pipelined_ms = e0.elapsed_time(e1) / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+        host.copy_(res, non_blocking=True)
+        stream.synchronize()
+    synced_ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert int(host[0]) == planted_L
+    return {
+        "full_step": {
+            "workload": "16 layers x (24 q / 4 kv heads, head_dim 256, 32768 Q4_0 rows, budget-22 tree) + acceptance "
+                        "over 23x152000 logits",
+            "steps_per_s_pipelined": 1e3 / pipelined_ms,
+            "ms_per_step_pipelined": pipelined_ms,
+            "steps_per_s_with_host_sync": 1e3 / synced_ms,
+            "ms_per_step_with_host_sync": synced_ms,
+            "kv_gbps": 16 * 2 * 4 * 32768 * 144 / (pipelined_ms * 1e-3) / 1e9,
+        }
+    }
 
 
 def cpu_baseline(inp, logits, parent, tokens, n_rows):

@@ -18,10 +18,10 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
 
 // Splits are sized so one launch fills the device with about one workgroup
-// per compute unit, but never below kMinChunks chunks (256 keys) per split:
-// a split's fixed cost (Q fragments, writing its partial state) has to be
-// amortised over its keys.
-constexpr int kMinChunks = 4;
+// per compute unit, down to one chunk per split: a split's fixed cost (Q
+// fragments, pipeline fill, writing its partial state) is paid in parallel,
+// which beats fewer, longer splits while the device is not full.
+constexpr int kMinChunks = 1;
 
 static int check_tree(int n, const int32_t *parent)
 {
