@@ -76,6 +76,7 @@ def test_bad_trees_rejected(L, parent, code):
     (dict(scale=-0.1), -1),
     (dict(ts=35), -3),             # token stride below the row size
     (dict(ts=38), -4),             # Q4_0 strides must be multiples of 4
+    (dict(ts=(1 << 24) + 4, hs=0), -3),  # row offsets inside a chunk must fit 32 bits
     (dict(kv=tv.TV_KV_F16, ts=136, hs=136 * 256), -4),  # F16 strides: multiples of 16
 ])
 def test_bad_shapes_rejected(L, kw, code):
