@@ -119,7 +119,8 @@ typedef struct tv_attn_ptrs {
 
 /*
  * Device workspace (bytes) tree_verify_attn needs for `d`: partial softmax
- * states of the key-range splits. 0 when `d` is invalid or no split is
+ * states of the key-range splits (per split and output row, the normalised
+ * partial output in fp16 and the log2 of its softmax denominator in fp32). 0 when `d` is invalid or no split is
  * needed (n_ctx == 0 after the window). Depends on the device's compute-unit
  * count, so query it for the device the call will run on (the current one).
  */

@@ -107,7 +107,8 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
 size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p)
 {
     const size_t NR = (size_t)d->n_nodes * d->n_q_heads;
-    return (size_t)p.S * NR * ((size_t)d->head_dim + 2) * sizeof(float);
+    // fp16 normalised outputs [S][NR][D], then fp32 log2 denominators [S][NR]
+    return (size_t)p.S * NR * ((size_t)d->head_dim * 2 + sizeof(float));
 }
 
 int device_cu_count(int *n_cu)

@@ -412,8 +412,8 @@ struct MergeArgs {
     const _Float16 *q;
     const _Float16 *k_tree;
     const _Float16 *v_tree;
-    const float *ws_o;
-    const float *ws_ml;
+    const _Float16 *ws_o;
+    const float *ws_m;
     float *out;
     int32_t NR;
     int32_t H_q;
@@ -433,8 +433,8 @@ struct MergeArgs {
     uint64_t anc[TV_MAX_NODES];
 };
 
-// Values d0 .. d0+n-1 (n <= 4, inside one 32-wide block) of one cache row,
-// decoded exactly in fp32.
+// Values d0 .. d0+n-1 (inside one 32-wide block) of one cache row, decoded
+// exactly in fp32.
 template <int N>
 __device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, int d0, float (&out)[N])
 {
@@ -457,17 +457,21 @@ __device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, in
 
 // One workgroup of 256 threads per output row (node i, query head h), in
 // three rounds of independent loads:
-//   1. thread (split group sg, d-quad dq) loads the partial states of its
+//   1. thread (split group sg, d-octet dq) loads the partial states of its
 //      splits s = sg, sg + NGR, ... and folds them against their own maximum;
 //      at the same time the threads score the row's extra keys (its tree
 //      ancestors, then the window's tail rows), KL lanes per key;
 //   2. the maximum over splits and extra keys;
 //   3. the extra keys' V rows are spread over the split groups; the groups'
 //      sums meet in LDS.
+// A split's weight is 2^(lse_s - m*) with lse_s the log2 of its softmax
+// denominator, an extra key's 2^(score - m*); the output is the weighted sum
+// of the splits' normalised outputs and the keys' V rows over the sum of the
+// weights.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 {
-    constexpr int QD = D / 4;       // d-quads per row
+    constexpr int QD = D / 8;       // d-octets per row
     constexpr int NGR = 256 / QD;   // split groups
     constexpr int KL = 16;          // lanes per extra key
     constexpr int KPT = D / KL;     // values per lane of a key's dot product
@@ -492,40 +496,38 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     // ---- round 1a: this thread's splits, folded against their maximum
     const int dq = t % QD, sg = t / QD;
     float ms = kNegBig;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
-    {
-        float mv[SMAX], lv[SMAX];
-        f4 ov[SMAX];
-        for (int s0 = sg; s0 < a.S; s0 += NGR * SMAX) {
+    for (int s0 = sg; s0 < a.S; s0 += NGR * SMAX) {
+        float mv[SMAX];
+        h8 ov[SMAX];
 #pragma unroll
-            for (int k = 0; k < SMAX; ++k) {
-                const int s = s0 + NGR * k;
-                if (s < a.S) {
-                    const int64_t base = (int64_t)s * a.NR + row;
-                    mv[k] = a.ws_ml[2 * base];
-                    lv[k] = a.ws_ml[2 * base + 1];
-                    ov[k] = *(const f4 *)(a.ws_o + base * D + 4 * dq);
-                } else {
-                    mv[k] = kNegBig;
-                    lv[k] = 0.f;
-                    ov[k] = (f4){0.f, 0.f, 0.f, 0.f};
-                }
+        for (int k = 0; k < SMAX; ++k) {
+            const int s = s0 + NGR * k;
+            if (s < a.S) {
+                const int64_t base = (int64_t)s * a.NR + row;
+                mv[k] = a.ws_m[base];
+                ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
+            } else {
+                mv[k] = kNegBig;
+                ov[k] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
             }
-            float mb = ms;
-#pragma unroll
-            for (int k = 0; k < SMAX; ++k) mb = fmaxf(mb, mv[k]);
-            const float r = exp2f(ms - mb);
-            acc *= r;
-            L *= r;
-#pragma unroll
-            for (int k = 0; k < SMAX; ++k) {
-                const float f = exp2f(mv[k] - mb);
-                L = __builtin_fmaf(f, lv[k], L);
-                acc += f * ov[k];
-            }
-            ms = mb;
         }
+        float mb = ms;
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) mb = fmaxf(mb, mv[k]);
+        const float r = exp2f(ms - mb);
+        L *= r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= r;
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const float f = exp2f(mv[k] - mb);
+            L += f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, (float)ov[k][e], acc[e]);
+        }
+        ms = mb;
     }
     // ---- round 1b: scores of the extra keys (ancestors, then tail rows)
     float mk = -INFINITY;
@@ -572,41 +574,40 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     for (int k = 0; k < NGR; ++k) mstar = fmaxf(mstar, red_s[k]);
     {
         const float r = exp2f(ms - mstar);
-        acc *= r;
         L *= r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= r;
     }
     // ---- round 3: the extra keys' V rows, spread over the split groups
     for (int kk = sg; kk < nk; kk += NGR) {
         const float f = exp2f(sk[kk] - mstar);
         L += f;
-        float vv[4];
+        float vv[8];
         if (kk < na) {
             uint64_t mm = anc;
             for (int r = 0; r < kk; ++r) mm &= mm - 1;
             const int j = __builtin_ctzll(mm);
-            const _Float16 *vr = a.v_tree + ((int64_t)j * a.H_kv + g) * D + 4 * dq;
+            const h8 vr = *(const h8 *)(a.v_tree + ((int64_t)j * a.H_kv + g) * D + 8 * dq);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) vv[p] = (float)vr[p];
+            for (int p = 0; p < 8; ++p) vv[p] = (float)vr[p];
         } else {
-            cache_values<4>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 4 * dq, vv);
+            cache_values<8>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 8 * dq, vv);
         }
-        acc.x = __builtin_fmaf(f, vv[0], acc.x);
-        acc.y = __builtin_fmaf(f, vv[1], acc.y);
-        acc.z = __builtin_fmaf(f, vv[2], acc.z);
-        acc.w = __builtin_fmaf(f, vv[3], acc.w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, vv[e], acc[e]);
     }
-    *(f4 *)&acc_s[sg][4 * dq] = acc;
+    *(f4 *)&acc_s[sg][8 * dq] = (f4){acc[0], acc[1], acc[2], acc[3]};
+    *(f4 *)&acc_s[sg][8 * dq + 4] = (f4){acc[4], acc[5], acc[6], acc[7]};
     if (dq == 0) l_s[sg] = L;
     __syncthreads();
-    if (t < QD) {
-        f4 sum = *(const f4 *)&acc_s[0][4 * t];
-        float Ls = l_s[0];
+    if (t < D) {
+        float sum = 0.f, Ls = 0.f;
 #pragma unroll
-        for (int k = 1; k < NGR; ++k) {
-            sum += *(const f4 *)&acc_s[k][4 * t];
+        for (int k = 0; k < NGR; ++k) {
+            sum += acc_s[k][t];
             Ls += l_s[k];
         }
-        *(f4 *)(a.out + (int64_t)row * D + 4 * t) = sum * (1.0f / Ls);
+        a.out[(int64_t)row * D + t] = sum / Ls;
     }
 }
 
@@ -644,8 +645,8 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
     const int G = Hq / Hkv;
     const int NR = n * Hq;
     const float c = d->scale * 1.4426950408889634f;
-    float *ws_o = (float *)ws;
-    float *ws_ml = ws_o + (size_t)plan.S * NR * D;
+    _Float16 *ws_o = (_Float16 *)ws;
+    float *ws_m = (float *)(ws_o + (size_t)plan.S * NR * D);
 
     if (plan.S > 0) {
         SplitArgs a;
@@ -655,7 +656,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         a.head_stride = d->kv_head_stride;
         a.q = (const _Float16 *)p->q;
         a.ws_o = ws_o;
-        a.ws_ml = ws_ml;
+        a.ws_m = ws_m;
         a.s0 = plan.s0;
         a.key_end = plan.s0 + plan.R;
         a.n_chunks = plan.n_chunks;
@@ -677,7 +678,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
     mg.k_tree = (const _Float16 *)p->k_tree;
     mg.v_tree = (const _Float16 *)p->v_tree;
     mg.ws_o = ws_o;
-    mg.ws_ml = ws_ml;
+    mg.ws_m = ws_m;
     mg.out = p->out;
     mg.NR = NR;
     mg.H_q = Hq;

@@ -30,8 +30,8 @@ struct SplitArgs {
     int64_t tok_stride;
     int64_t head_stride;
     const _Float16 *q;
-    float *ws_o;   // [S][NR][D] unnormalised partial outputs
-    float *ws_ml;  // [S][NR][2] running max (log2 units) and row sum
+    _Float16 *ws_o;  // [S][NR][D] partial outputs, each divided by its row sum
+    float *ws_m;     // [S][NR] log2 of the partial's softmax denominator
     int64_t s0;
     int64_t key_end;  // end of the rows covered by whole chunks
     int64_t n_chunks;
@@ -58,6 +58,20 @@ __device__ __forceinline__ float add_pair(h2 p, float acc)
 {
     const fp16x2 one = {(__fp16)1.0f, (__fp16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, p), one, acc, false);
+}
+
+// A split's partial state leaves the kernel normalised: O / l in fp16 (a
+// convex combination of V rows, so it has the range of V) and the log2 of its
+// denominator m + log2(l), which is all a log-sum-exp merge needs. A row with
+// no keys gets a zero output and a weight of 2^-1e30.
+__device__ __forceinline__ float partial_lse2(float m, float l)
+{
+    return l > 0.f ? m + __builtin_amdgcn_logf(l) : kNegBig;
+}
+
+__device__ __forceinline__ void store_h4(_Float16 *p, f4 v, float inv)
+{
+    *(h4 *)p = __builtin_convertvector(v * inv, h4);
 }
 
 // 8 Q4_0 codes packed in one dword (code bytes 4k..4k+3 of a block) -> the
@@ -186,8 +200,8 @@ __device__ __forceinline__ void load_q_frags(const SplitArgs &a, int gkv, int ti
     }
 }
 
-// Writes the split's partial state (running max in log2 units, row sum,
-// unnormalised output) of every query row. Own tiles go straight to the
+// Writes the split's partial state (normalised output, log2 denominator) of
+// every query row. Own tiles go straight to the
 // workspace; the four waves' partial states of a shared tile are combined
 // through LDS (`scratch`, at least scratch_bytes long, free once called).
 template <int D, int NOWN, int NSH>
@@ -204,13 +218,11 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
         if (tile[k] < t_end && r < a.M) {
             const int node = r / a.G, h = gkv * a.G + r % a.G;
             const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-            float *op = a.ws_o + row * D + 4 * grp;
+            _Float16 *op = a.ws_o + row * D + 4 * grp;
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) *(f4 *)(op + 16 * dt) = o[k][dt];
-            if (grp == 0) {
-                a.ws_ml[2 * row] = m[k];
-                a.ws_ml[2 * row + 1] = lt;
-            }
+            for (int dt = 0; dt < NDT; ++dt) store_h4(op + 16 * dt, o[k][dt], inv);
+            if (grp == 0) a.ws_m[row] = partial_lse2(m[k], lt);
         }
     }
     if constexpr (NSH > 0) {
@@ -251,11 +263,8 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
                 }
                 const int node = r / a.G, h = gkv * a.G + r % a.G;
                 const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-                a.ws_o[row * D + d] = acc;
-                if (d == 0) {
-                    a.ws_ml[2 * row] = mx;
-                    a.ws_ml[2 * row + 1] = lsum;
-                }
+                a.ws_o[row * D + d] = (_Float16)(lsum > 0.f ? acc / lsum : 0.f);
+                if (d == 0) a.ws_m[row] = partial_lse2(mx, lsum);
             }
         }
     }

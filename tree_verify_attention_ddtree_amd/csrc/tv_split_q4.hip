@@ -442,18 +442,16 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         if (tile[k] < tm.t_end && r < a.M) {
             const int node = r / a.G, h = gkv * a.G + r % a.G;
             const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-            float *op = a.ws_o + row * D + 4 * grp;
+            _Float16 *op = a.ws_o + row * D + 4 * grp;
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
             if (k < NOWN) {
 #pragma unroll
-                for (int j = 0; j < NDT; ++j) *(f4 *)(op + 16 * ((j + rot) & (NDT - 1))) = o[k < NOWN ? k : 0][j];
+                for (int j = 0; j < NDT; ++j) store_h4(op + 16 * ((j + rot) & (NDT - 1)), o[k < NOWN ? k : 0][j], inv);
             } else {
 #pragma unroll
-                for (int j = 0; j < NDQ; ++j) *(f4 *)(op + 16 * (j + rot)) = osh[k >= NOWN ? k - NOWN : 0][j];
+                for (int j = 0; j < NDQ; ++j) store_h4(op + 16 * (j + rot), osh[k >= NOWN ? k - NOWN : 0][j], inv);
             }
-            if (grp == 0 && (k < NOWN || w == 0)) {
-                a.ws_ml[2 * row] = m[k];
-                a.ws_ml[2 * row + 1] = lt;
-            }
+            if (grp == 0 && (k < NOWN || w == 0)) a.ws_m[row] = partial_lse2(m[k], lt);
         }
     }
 }
