@@ -34,8 +34,11 @@ METRIC = "tree-verify steps/s and effective KV GB/s (% HBM peak), budget 22 @128
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # a cold device needs about a hundred milliseconds of work to reach its
+    # steady clocks; the long timed bracket lets the host run ahead of the
+    # device by a deep queue, so a brief host-side stall does not idle it
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="long", choices=["long", "27b", "window"])
     ap.add_argument("--kv", default="q4_0", choices=["q4_0", "f16"])
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9, help="KV bytes the copies span at least")
