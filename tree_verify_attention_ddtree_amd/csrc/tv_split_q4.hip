@@ -87,6 +87,17 @@ __device__ __forceinline__ void split_half_block(const u32 *r, int b, _Float16 &
     c1 = odd ? r[3] : __builtin_amdgcn_alignbyte(r[3], r[2], 2);
 }
 
+typedef u32 u3v __attribute__((ext_vector_type(3)));
+typedef u32 u4v __attribute__((ext_vector_type(4)));
+
+// Raw-buffer descriptor over one chunk of cache rows: the base moves with the
+// chunk (scalar arithmetic), the per-lane offsets stay constant, and reads
+// past num_records return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint8_t *base, u32 bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
 template <int D>
 struct Q4Loader {
     using Sh = Q4Share<D>;
@@ -94,9 +105,11 @@ struct Q4Loader {
     const uint8_t *kbase;  // K cache of this KV head
     const uint8_t *vbase;
     int64_t tok_stride;
+    u32 chunk_bytes;   // 64 rows
     int kk, u;         // K: key in chunk, half-block group
     int kg, vb, vh;    // V: key group, block, half
-    u32 krow, vrow;    // byte offsets of this thread's first K / V row inside a chunk
+    u32 krow;          // byte offset of this thread's K row inside a chunk
+    u32 voff_s, voff_w;  // V: offsets of the scale dword and the code window of the first key
     u32 rk[Sh::RAWK];
     u32 rv[Sh::RAWV];
 
@@ -105,34 +118,66 @@ struct Q4Loader {
         kbase = a.k_cache + (int64_t)gkv * a.head_stride;
         vbase = a.v_cache + (int64_t)gkv * a.head_stride;
         tok_stride = a.tok_stride;
+        chunk_bytes = (u32)(kChunk * a.tok_stride);
         kk = tid & 63;
-        u = tid >> 6;
+        u = __builtin_amdgcn_readfirstlane(tid >> 6);
         kg = tid % Sh::KG;
         const int rest = tid / Sh::KG;
         vb = rest % NB;
         vh = rest / NB;
         krow = (u32)(kk * tok_stride);
-        vrow = (u32)(Sh::NKV * kg * tok_stride);
+        const u32 vrow = (u32)(Sh::NKV * kg * tok_stride);
+        voff_s = vrow + (u32)scale_dword_off(vb);
+        voff_w = vrow + (u32)window_off(vb, vh);
     }
 
     // Every key of a chunk is a committed row (the tail of the window that
-    // does not fill a chunk is left to the merge kernel), so no bounds checks.
-    // The chunk base is uniform; per-thread offsets are 32-bit.
+    // does not fill a chunk is left to the merge kernel), so no bounds checks
+    // beyond the descriptor's.
     __device__ __forceinline__ void load_k(int64_t chunk_row)
     {
-        const uint8_t *cb = kbase + chunk_row * tok_stride;
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(kbase + chunk_row * tok_stride, chunk_bytes);
+        if constexpr (Sh::HB == 4) {
+            // blocks 2u and 2u+1: 36 contiguous bytes from a 4-byte aligned start
+            const int so = 36 * u;
+            const u4v d0 = __builtin_amdgcn_raw_buffer_load_b128(r, krow, so, 0);
+            const u4v d1 = __builtin_amdgcn_raw_buffer_load_b128(r, krow, so + 16, 0);
+            const u32 d8 = __builtin_amdgcn_raw_buffer_load_b32(r, krow, so + 32, 0);
+            const u32 d[9] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w, d8};
+            // half-block t: scale dword, then the 3-dword window of its codes
+            const int sc[4] = {0, 0, 4, 4}, wi[4] = {0, 2, 4, 6};
 #pragma unroll
-        for (int t = 0; t < Sh::HB; ++t) {
-            const int j = u * Sh::HB + t;
-            load_half_block(cb + krow, j >> 1, j & 1, rk + 4 * t);
+            for (int t = 0; t < 4; ++t) {
+                rk[4 * t] = d[sc[t]];
+                rk[4 * t + 1] = d[wi[t]];
+                rk[4 * t + 2] = d[wi[t] + 1];
+                rk[4 * t + 3] = d[wi[t] + 2];
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < Sh::HB; ++t) {
+                const int j = u * Sh::HB + t, b = j >> 1, h = j & 1;
+                rk[4 * t] = __builtin_amdgcn_raw_buffer_load_b32(r, krow, scale_dword_off(b), 0);
+                const u3v w = __builtin_amdgcn_raw_buffer_load_b96(r, krow, window_off(b, h), 0);
+                rk[4 * t + 1] = w.x;
+                rk[4 * t + 2] = w.y;
+                rk[4 * t + 3] = w.z;
+            }
         }
     }
 
     __device__ __forceinline__ void load_v(int64_t chunk_row)
     {
-        const uint8_t *cb = vbase + chunk_row * tok_stride;
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(vbase + chunk_row * tok_stride, chunk_bytes);
 #pragma unroll
-        for (int q = 0; q < Sh::NKV; ++q) load_half_block(cb + vrow + (u32)(q * tok_stride), vb, vh, rv + 4 * q);
+        for (int q = 0; q < Sh::NKV; ++q) {
+            const int so = (int)(q * tok_stride);
+            rv[4 * q] = __builtin_amdgcn_raw_buffer_load_b32(r, voff_s, so, 0);
+            const u3v w = __builtin_amdgcn_raw_buffer_load_b96(r, voff_w, so, 0);
+            rv[4 * q + 1] = w.x;
+            rv[4 * q + 2] = w.y;
+            rv[4 * q + 3] = w.z;
+        }
     }
 
     // K piece j (0..NB-1): code dword j of this thread -> one 16-byte store
