@@ -13,7 +13,8 @@
 // largest value with the smallest index; NaN maps to the lowest code and -0 to
 // the code of +0.
 // Kernel 2 (finish_walk): one wave, lane i = node i: reduces the slices of
-// row i, then finds the accepted path with wave-wide pointer jumping.
+// row i, then finds the accepted path from ballots over the nodes' ancestor
+// masks (built on the host from the parent array).
 
 #include "tv_internal.h"
 
@@ -51,20 +52,31 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t v)
 __global__ void __launch_bounds__(kAccThreads) argmax_partial(const float *logits, int vocab, int n_slices,
                                                               uint64_t *part)
 {
+    constexpr int PER = kSliceFloats / (4 * kAccThreads);  // 16-byte loads per thread
     const int row = blockIdx.y, sl = blockIdx.x;
     const int64_t lo = (int64_t)sl * kSliceFloats;
     const int64_t hi = lo + kSliceFloats < vocab ? lo + kSliceFloats : vocab;
     const float *r = logits + (int64_t)row * vocab;
-    uint64_t best = 0;
-    // 16-byte loads where the row allows them; rows start 16-byte aligned
-    // only when vocab is a multiple of 4.
+    uint64_t best = 0;  // below every key
+    // 16-byte loads where the row allows them (rows start 16-byte aligned
+    // only when vocab is a multiple of 4); all of a thread's loads are issued
+    // before the first compare.
     if ((vocab & 3) == 0) {
-        for (int64_t v = lo + 4 * threadIdx.x; v < hi; v += 4 * kAccThreads) {
-            const float4 x = *(const float4 *)(r + v);
-            best = umax64(best, pack_key(x.x, (uint32_t)v));
-            best = umax64(best, pack_key(x.y, (uint32_t)v + 1));
-            best = umax64(best, pack_key(x.z, (uint32_t)v + 2));
-            best = umax64(best, pack_key(x.w, (uint32_t)v + 3));
+        float4 x[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
+            x[k] = v < hi ? *(const float4 *)(r + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
+            if (v < hi) {
+                best = umax64(best, pack_key(x[k].x, (uint32_t)v));
+                best = umax64(best, pack_key(x[k].y, (uint32_t)v + 1));
+                best = umax64(best, pack_key(x[k].z, (uint32_t)v + 2));
+                best = umax64(best, pack_key(x[k].w, (uint32_t)v + 3));
+            }
         }
     } else {
         for (int64_t v = lo + threadIdx.x; v < hi; v += kAccThreads) best = umax64(best, pack_key(r[v], (uint32_t)v));
@@ -88,34 +100,28 @@ struct WalkArgs {
     int32_t n_slices;
     int32_t parent[TV_MAX_NODES];
     int32_t tokens[TV_MAX_NODES];
+    uint64_t anc[TV_MAX_NODES];  // ancestor-or-self mask of each node
 };
 
-__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src)
-{
-    const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// One wave; lane i stands for tree node i.
+// One wave; lane i stands for tree node i (its parent, token and
+// ancestor-or-self mask come from the kernel arguments).
 //   1. a[i]: lane i reduces the slice maxima of row i.
-//   2. Pointer jumping over parents (6 rounds cover depth 63): depth, whether
-//      every edge of the root path matches (child token == parent's argmax),
-//      and the ancestor-or-self bitmask.
-//   3. The deepest matched nodes mark their root paths; the descent from the
+//   2. Node i matches when its token equals its parent's argmax; it is on an
+//      accepted path when every node of its root path matches, i.e. its
+//      ancestor mask lies inside the ballot of matching nodes.
+//   3. The deepest such nodes mark their root paths; the descent from the
 //      root takes, at every level, the smallest child on a marked path, which
 //      is the lexicographically smallest of the longest accepted paths.
+// Only the parent's argmax crosses lanes through LDS; the rest are ballots
+// and lane reads of uniform indices.
 __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
 {
     const int lane = threadIdx.x;
     const int n = a.n;
-    int par = -1, tok = -1;
-#pragma unroll
-    for (int i = 0; i < TV_MAX_NODES; ++i)
-        if (lane == i) {
-            par = a.parent[i];
-            tok = a.tokens[i];
-        }
     const bool live = lane < n;
+    const int par = live ? a.parent[lane] : -1;
+    const int tok = live ? a.tokens[lane] : -1;
+    const uint64_t anc = live ? a.anc[lane] : 0ull;
 
     int am = 0;
     if (live) {
@@ -133,64 +139,60 @@ __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
         a.argmax_out[lane] = am;
     }
 
-    const int p0 = (live && lane > 0) ? par : lane;  // root and dead lanes point to themselves
-    const int am_parent = __shfl(am, p0);
-    bool ok = !live ? false : (lane == 0 ? true : tok == am_parent);
-    int nxt = p0;
-    int depth = (live && lane > 0) ? 1 : 0;
-    uint64_t msk = 1ull << lane;
+    const int am_parent = __shfl(am, (live && lane > 0) ? par : lane);
+    const bool matched = live && (lane == 0 || tok == am_parent);
+    const uint64_t M = __builtin_amdgcn_ballot_w64(matched);
+    const bool ok = live && (anc & ~M) == 0;
+    const int depth = __builtin_popcountll(anc) - 1;
+    // deepest accepted depth, one bit at a time from the top
+    int best = 0;
 #pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        const bool ok_n = __shfl((int)ok, nxt) != 0;
-        const int d_n = __shfl(depth, nxt);
-        const uint64_t m_n = shfl64(msk, nxt);
-        const int nxt_n = __shfl(nxt, nxt);
-        if (nxt != lane) {
-            ok = ok && ok_n;
-            depth += d_n;
-            msk |= m_n;
-        }
-        nxt = nxt_n;
+    for (int bit = 5; bit >= 0; --bit) {
+        const int cand = best | (1 << bit);
+        if (__builtin_amdgcn_ballot_w64(ok && depth >= cand)) best = cand;
     }
-    const bool matched = live && ok;
-    int best = matched ? depth : -1;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
-    uint64_t onpath = (matched && depth == best) ? msk : 0ull;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) onpath |= shfl64(onpath, lane ^ off);
-
-    // descent; lane k records the k-th node of the path
-    int u = 0, len = 1, mypath = lane == 0 ? 0 : -1;
+    // root paths of the deepest accepted nodes
+    uint64_t deepest = __builtin_amdgcn_ballot_w64(ok && depth == best);
+    uint64_t onpath = 0;
+    const uint32_t anc_lo = (uint32_t)anc, anc_hi = (uint32_t)(anc >> 32);
+    while (deepest) {
+        const int d = __builtin_ctzll(deepest);
+        deepest &= deepest - 1;
+        onpath |= ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(anc_hi, d) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane(anc_lo, d);
+    }
+    // descent from the root
+    int u = 0, n_acc = 0;
+    uint64_t chosen = 1ull;
     for (;;) {
         const uint64_t cand = __builtin_amdgcn_ballot_w64(live && lane > 0 && par == u && ((onpath >> lane) & 1));
         if (!cand) break;
         u = __builtin_ctzll(cand);
-        if (lane == len) mypath = u;
-        ++len;
+        chosen |= 1ull << u;
+        ++n_acc;
     }
-    const int n_acc = len - 1;
-    const int bonus = __shfl(am, u);
-    // every output position is written exactly once; the shuffles run with
-    // all lanes active
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        const int pos = lane + 64 * r;
-        const int jp = pos - 2;      // index into the path
-        const int je = pos - 2 - n;  // index into the emitted tokens
-        const int pj = __shfl(mypath, (jp >= 0 && jp < 64) ? jp : 0);
-        const int pe = __shfl(mypath, (je + 1 >= 0 && je + 1 < 64) ? je + 1 : 0);
-        const int te = __shfl(tok, (pe >= 0 && pe < 64) ? pe : 0);
-        int v;
-        if (pos == 0)
-            v = n_acc;
-        else if (pos == 1)
-            v = bonus;
-        else if (pos < 2 + n)
-            v = jp <= n_acc ? pj : -1;
-        else
-            v = je < n_acc ? te : (je == n_acc ? bonus : -1);
-        if (pos < 2 + 2 * n) a.result_out[pos] = v;
+    const int bonus = __builtin_amdgcn_readlane(am, u);
+    // result layout: [n_acc, bonus, path nodes (n, -1 padded), emitted tokens
+    // (n: the path's draft tokens, then the bonus, -1 padded)]. The nodes of
+    // the chosen path write their own entries; every other position is
+    // written by the lane of that index.
+    int32_t *res = a.result_out;
+    if ((chosen >> lane) & 1) {
+        res[2 + depth] = lane;
+        if (depth >= 1) res[2 + n + depth - 1] = tok;
+    }
+    for (int pos = lane; pos < 2 + 2 * n; pos += 64) {
+        if (pos == 0) {
+            res[0] = n_acc;
+        } else if (pos == 1) {
+            res[1] = bonus;
+        } else if (pos < 2 + n) {
+            if (pos - 2 > n_acc) res[pos] = -1;
+        } else {
+            const int je = pos - 2 - n;
+            if (je == n_acc) res[pos] = bonus;
+            else if (je > n_acc) res[pos] = -1;
+        }
     }
 }
 
@@ -214,6 +216,10 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
     for (int i = 0; i < TV_MAX_NODES; ++i) {
         w.parent[i] = i < n ? parent[i] : -1;
         w.tokens[i] = i < n ? tokens[i] : -1;
+        uint64_t m = 0;
+        if (i < n)
+            for (int v = i; v >= 0; v = parent[v]) m |= 1ull << v;
+        w.anc[i] = m;
     }
     hipLaunchKernelGGL(finish_walk, dim3(1), dim3(64), 0, stream, w);
     if (hipGetLastError() != hipSuccess) return TV_E_HIP;
