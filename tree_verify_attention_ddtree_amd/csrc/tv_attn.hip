@@ -462,8 +462,9 @@ __device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, in
 //      at the same time the threads score the row's extra keys (its tree
 //      ancestors, then the window's tail rows), KL lanes per key;
 //   2. the maximum over splits and extra keys;
-//   3. the extra keys' V rows are spread over the split groups; the groups'
-//      sums meet in LDS.
+//   3. the extra keys' V rows are spread over the split groups (the first
+//      VPF of each group are loaded during round 1, as they do not depend on
+//      the scores); the groups' sums meet in LDS.
 // A split's weight is 2^(lse_s - m*) with lse_s the log2 of its softmax
 // denominator, an extra key's 2^(score - m*); the output is the weighted sum
 // of the splits' normalised outputs and the keys' V rows over the sum of the
@@ -477,6 +478,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     constexpr int KPT = D / KL;     // values per lane of a key's dot product
     constexpr int KPASS = 256 / KL; // extra keys per pass
     constexpr int SMAX = 8;         // splits per thread held in registers
+    constexpr int VPF = 2;          // extra keys per split group whose V is loaded early
     static_assert(32 % KPT == 0, "a lane's key slice lies inside one 32-value block");
     __shared__ float sk[TV_MAX_NODES + kChunk];
     __shared__ float red_s[NGR];
@@ -493,8 +495,28 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     const uint8_t *kh = a.k_cache + (int64_t)g * a.head_stride;
     const uint8_t *vh = a.v_cache + (int64_t)g * a.head_stride;
 
-    // ---- round 1a: this thread's splits, folded against their maximum
     const int dq = t % QD, sg = t / QD;
+    // V values of this group's first extra keys, requested before anything
+    // waits on memory
+    auto extra_v = [&](int kk, float (&vv)[8]) {
+        if (kk < na) {
+            uint64_t mm = anc;
+            for (int r = 0; r < kk; ++r) mm &= mm - 1;
+            const int j = __builtin_ctzll(mm);
+            const h8 vr = *(const h8 *)(a.v_tree + ((int64_t)j * a.H_kv + g) * D + 8 * dq);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) vv[p] = (float)vr[p];
+        } else {
+            cache_values<8>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 8 * dq, vv);
+        }
+    };
+    float vpf[VPF][8];
+#pragma unroll
+    for (int j = 0; j < VPF; ++j) {
+        if (sg + NGR * j < nk) extra_v(sg + NGR * j, vpf[j]);
+    }
+
+    // ---- round 1a: this thread's splits, folded against their maximum
     float ms = kNegBig;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
@@ -579,20 +601,21 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
         for (int e = 0; e < 8; ++e) acc[e] *= r;
     }
     // ---- round 3: the extra keys' V rows, spread over the split groups
-    for (int kk = sg; kk < nk; kk += NGR) {
+#pragma unroll
+    for (int j = 0; j < VPF; ++j) {
+        const int kk = sg + NGR * j;
+        if (kk < nk) {
+            const float f = exp2f(sk[kk] - mstar);
+            L += f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, vpf[j][e], acc[e]);
+        }
+    }
+    for (int kk = sg + NGR * VPF; kk < nk; kk += NGR) {
         const float f = exp2f(sk[kk] - mstar);
         L += f;
         float vv[8];
-        if (kk < na) {
-            uint64_t mm = anc;
-            for (int r = 0; r < kk; ++r) mm &= mm - 1;
-            const int j = __builtin_ctzll(mm);
-            const h8 vr = *(const h8 *)(a.v_tree + ((int64_t)j * a.H_kv + g) * D + 8 * dq);
-#pragma unroll
-            for (int p = 0; p < 8; ++p) vv[p] = (float)vr[p];
-        } else {
-            cache_values<8>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 8 * dq, vv);
-        }
+        extra_v(kk, vv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, vv[e], acc[e]);
     }
