@@ -30,7 +30,9 @@ _lib = None
 
 def build() -> str:
     """Compile tvref.c into libtvref.so with gcc and OpenMP."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    # no contraction: the Q4_0 quantiser rounds x * id and the + 8.5 separately
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp",
+           "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -60,6 +62,14 @@ def lib():
         L.tvref_argmax_row.restype = i32
         L.tvref_accept.argtypes = [P, i32, i32, P, P, P, P]
         L.tvref_accept.restype = i32
+        L.tvref_float_to_half.argtypes = [ctypes.c_float]
+        L.tvref_float_to_half.restype = ctypes.c_uint16
+        L.tvref_q4_0_quantize_block.argtypes = [P, P]
+        L.tvref_q4_0_quantize_block.restype = None
+        L.tvref_q4_0_quantize_rows.argtypes = [P, i64, i32, P]
+        L.tvref_q4_0_quantize_rows.restype = None
+        L.tvref_commit.argtypes = [i32, i32, i32, i32, i64, i64, P, P, P, P, P, i64, i64]
+        L.tvref_commit.restype = i32
         _lib = L
     return _lib
 
@@ -148,3 +158,42 @@ def accept(logits: np.ndarray, parent, tokens):
     if rc != 0:
         raise ValueError(f"tvref_accept failed with {rc}")
     return am, res
+
+
+def float_to_half(x: float) -> int:
+    """fp16 bits of an fp32 value, rounded to nearest even."""
+    return int(lib().tvref_float_to_half(float(np.float32(x))))
+
+
+def q4_0_quantize(x: np.ndarray) -> np.ndarray:
+    """fp32 [..., D] (D a multiple of 32) -> Q4_0 bytes [..., 18*D/32], with
+    the quantiser reading documented in tvref.c."""
+    x = np.ascontiguousarray(x, np.float32)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    lead = x.shape[:-1]
+    nr = int(np.prod(lead)) if lead else 1
+    out = np.empty(lead + (18 * (D // 32),), np.uint8)
+    lib().tvref_q4_0_quantize_rows(_ptr(x), nr, D, _ptr(out))
+    return out
+
+
+def commit(result, k_tree, v_tree, k_cache, v_cache, n_ctx):
+    """Oracle KV commit of the accepted path into head-major caches.
+
+    result: int32 [2 + 2n] from the acceptance; k_tree, v_tree: fp16 [n][H_kv][D];
+    k_cache, v_cache: [H_kv][capacity][row] (uint8 Q4_0 rows or fp16 values).
+    Returns new (k_cache, v_cache) arrays; the inputs are not modified.
+    """
+    result = np.ascontiguousarray(result, np.int32)
+    kt = np.ascontiguousarray(k_tree, np.float16)
+    vt = np.ascontiguousarray(v_tree, np.float16)
+    n, Hkv, D = kt.shape
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    kv = KV_Q4_0 if kc.dtype == np.uint8 else KV_F16
+    rc = lib().tvref_commit(n, Hkv, D, kv, int(n_ctx), kc.shape[1], _ptr(result), _ptr(kt.view(np.uint16)),
+                            _ptr(vt.view(np.uint16)), _ptr(kc), _ptr(vc), kc.strides[1], kc.strides[0])
+    if rc != 0:
+        raise ValueError(f"tvref_commit failed with {rc}")
+    return kc, vc

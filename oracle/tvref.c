@@ -287,3 +287,125 @@ int tvref_accept(const float *logits, int n, int vocab, const int32_t *parent, c
     free(best);
     return TVREF_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * KV commit of the accepted path: after acceptance the root and the accepted
+ * nodes become committed tokens, so their K and V rows are appended to the
+ * cache (the pages keep the target's cache in Q4_0 or F16; they name Q4_0
+ * but give no quantiser).
+ *
+ * Reading of the Q4_0 quantiser, per 32-value block, all in fp32 (the
+ * precision in which the GPU kernel takes the same integer decisions):
+ *   m     = the value of largest magnitude (the first one on ties);
+ *   d     = m / -8, stored as fp16 rounded to nearest, ties to even;
+ *   id    = 1 / d (0 when d == 0);
+ *   c     = x * id rounded to fp32, then + 8.5 rounded to fp32 (two
+ *           roundings, no fused multiply-add);
+ *   code  = 15 if c >= 15, floor(c) if 0 <= c < 15, and 0 otherwise (which
+ *           includes NaN).
+ * So the element of largest magnitude gets code 0 and decodes to m exactly
+ * whenever d is exact in fp16, and every other value lands on the nearest
+ * code, ties upward.
+ * ------------------------------------------------------------------------ */
+
+/* IEEE binary32 -> binary16, round to nearest, ties to even; overflow gives
+ * infinity, NaN stays NaN (quiet). From the bit layouts. */
+uint16_t tvref_float_to_half(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, sizeof x);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const uint32_t ax = x & 0x7fffffffu;
+    if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x0200u : 0u));
+    if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u); /* |f| >= 65520 */
+    if (ax >= 0x38800000u) {                                  /* |f| >= 2^-14: normal half */
+        const uint32_t m = ax - 0x38000000u;                  /* exponent bias 127 -> 15 */
+        const uint32_t r = m + 0x0fffu + ((m >> 13) & 1u);    /* drop 13 fraction bits, ties to even */
+        return (uint16_t)(sign | (r >> 13));
+    }
+    if (ax <= 0x33000000u) return (uint16_t)sign; /* |f| <= 2^-25: rounds to zero */
+    /* subnormal half: round |f| / 2^-24 to an integer, ties to even */
+    const uint32_t e = ax >> 23;
+    const uint32_t man = (ax & 0x7fffffu) | 0x800000u; /* |f| = man * 2^(e - 150) */
+    const uint32_t s = 126u - e;                       /* |f| / 2^-24 = man >> s */
+    uint32_t q = man >> s;
+    const uint32_t rem = man & ((1u << s) - 1u), half = 1u << (s - 1u);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return (uint16_t)(sign | q);
+}
+
+static int q4_code(float x, float id)
+{
+    const float p = x * id;
+    const float c = p + 8.5f;
+    if (c >= 15.0f) return 15;
+    if (c >= 0.0f) return (int)floorf(c);
+    return 0;
+}
+
+/* 32 fp32 values -> one 18-byte Q4_0 block. */
+void tvref_q4_0_quantize_block(const float *x, uint8_t *out)
+{
+    float amax = 0.0f, m = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        const float a = fabsf(x[j]);
+        if (amax < a) {
+            amax = a;
+            m = x[j];
+        }
+    }
+    const float d = m / -8.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;
+    const uint16_t hd = tvref_float_to_half(d);
+    out[0] = (uint8_t)(hd & 0xffu);
+    out[1] = (uint8_t)(hd >> 8);
+    for (int j = 0; j < 16; ++j) out[2 + j] = (uint8_t)(q4_code(x[j], id) | (q4_code(x[j + 16], id) << 4));
+}
+
+/* n_rows rows of D fp32 values -> n_rows Q4_0 rows of 18*D/32 bytes. */
+void tvref_q4_0_quantize_rows(const float *x, int64_t n_rows, int D, uint8_t *out)
+{
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int b = 0; b < D / 32; ++b) tvref_q4_0_quantize_block(x + r * D + 32 * b, out + r * (18 * (D / 32)) + 18 * b);
+}
+
+/*
+ * Appends the accepted path to one layer's caches.
+ *   result   the acceptance result (int32 [2 + 2n]): n_acc = result[0], the
+ *            path's nodes result[2 .. 2 + n_acc], root first;
+ *   k_tree, v_tree  fp16 bits [n][H_kv][D], the tree nodes' K and V rows;
+ *   k_cache, v_cache  rows addressed as head * head_stride + row * tok_stride
+ *            (bytes), capacity rows per head; F16 rows are copied, Q4_0 rows
+ *            quantised with the reading above.
+ * Path node path[r] goes to cache row n_ctx + r of every KV head, for
+ * r = 0 .. n_acc; no other row is written.
+ */
+int tvref_commit(int n, int H_kv, int D, int kv_type, int64_t n_ctx, int64_t capacity, const int32_t *result,
+                 const uint16_t *k_tree, const uint16_t *v_tree, uint8_t *k_cache, uint8_t *v_cache,
+                 int64_t tok_stride, int64_t head_stride)
+{
+    if (n < 1 || n > 64 || H_kv < 1 || (D != 64 && D != 128 && D != 256)) return TVREF_ESHAPE;
+    if (kv_type != TVREF_KV_F16 && kv_type != TVREF_KV_Q4_0) return TVREF_EARG;
+    if (n_ctx < 0 || n_ctx + n > capacity) return TVREF_ESHAPE;
+    const int n_acc = result[0];
+    if (n_acc < 0 || n_acc >= n) return TVREF_EARG;
+    for (int r = 0; r <= n_acc; ++r)
+        if (result[2 + r] < 0 || result[2 + r] >= n) return TVREF_EARG;
+    float x[256];
+    for (int r = 0; r <= n_acc; ++r) {
+        const int node = result[2 + r];
+        for (int g = 0; g < H_kv; ++g) {
+            for (int kv = 0; kv < 2; ++kv) {
+                const uint16_t *src = (kv ? v_tree : k_tree) + ((int64_t)node * H_kv + g) * D;
+                uint8_t *dst = (kv ? v_cache : k_cache) + g * head_stride + (n_ctx + r) * tok_stride;
+                if (kv_type == TVREF_KV_F16) {
+                    memcpy(dst, src, (size_t)D * 2);
+                } else {
+                    for (int d = 0; d < D; ++d) x[d] = (float)tvref_half_to_double(src[d]);
+                    for (int b = 0; b < D / 32; ++b) tvref_q4_0_quantize_block(x + 32 * b, dst + 18 * b);
+                }
+            }
+        }
+    }
+    return TVREF_OK;
+}
