@@ -297,7 +297,8 @@ int tvref_accept(const float *logits, int n, int vocab, const int32_t *parent, c
  * Reading of the Q4_0 quantiser, per 32-value block, all in fp32 (the
  * precision in which the GPU kernel takes the same integer decisions):
  *   m     = the value of largest magnitude (the first one on ties);
- *   d     = m / -8, stored as fp16 rounded to nearest, ties to even;
+ *   d     = m / -8, stored as fp16 rounded to nearest, ties to even (a block
+ *           of zeros, m = 0, stores the scale +0);
  *   id    = 1 / d (0 when d == 0);
  *   c     = x * id rounded to fp32, then + 8.5 rounded to fp32 (two
  *           roundings, no fused multiply-add);
@@ -354,7 +355,7 @@ void tvref_q4_0_quantize_block(const float *x, uint8_t *out)
             m = x[j];
         }
     }
-    const float d = m / -8.0f;
+    const float d = m != 0.0f ? m / -8.0f : 0.0f;
     const float id = d != 0.0f ? 1.0f / d : 0.0f;
     const uint16_t hd = tvref_float_to_half(d);
     out[0] = (uint8_t)(hd & 0xffu);

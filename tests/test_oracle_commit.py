@@ -111,9 +111,10 @@ def test_error_bound_random_blocks():
 
 def test_special_blocks():
     z = np.zeros(32, np.float32)
-    # d = 0 / -8 is -0 in IEEE arithmetic (fp16 0x8000); every code is 8, and
-    # every value decodes to zero
-    assert np.array_equal(oracle.q4_0_quantize(z), np.array([0x00, 0x80] + [0x88] * 16, np.uint8))
+    # a block of zeros stores the scale +0 (m / -8 alone would give -0) and
+    # code 8 everywhere; it decodes to zeros
+    assert np.array_equal(oracle.q4_0_quantize(z), np.array([0x00, 0x00] + [0x88] * 16, np.uint8))
+    assert np.array_equal(oracle.q4_0_quantize(-z), np.array([0x00, 0x00] + [0x88] * 16, np.uint8))
     assert not oracle.q4_0_dequant(oracle.q4_0_quantize(z), 32).any()
     one = z.copy()
     one[5] = 3.0  # d = -0.375 (fp16 0xB600); element 5 gets code 0, all others code 8
