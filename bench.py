@@ -244,23 +244,33 @@ def main():
 
 
 def full_step(tv, synth, dev, stream, steps):
-    """A whole verify step of a 16-layer model of the same head layout at
-    32K context: 16 tree-verify attention launches over 16 distinct Q4_0
-    layer caches (604 MB together), then the acceptance. Timed back to back
-    (pipelined) and with the step's result copied to the host and the stream
-    synchronised after every step, as a decode loop must."""
+    """A whole decode step of a 16-layer model of the same head layout at 32K
+    context: 16 tree-verify attention launches over 16 distinct Q4_0 layer
+    caches (604 MB together), the acceptance, then the KV commit of the
+    accepted path into each of the 16 caches (rows past n_ctx, so every step
+    reads the same context). Timed back to back (pipelined) and with the
+    step's result copied to the host and the stream synchronised after every
+    step, as a decode loop must."""
     import torch
     w = dict(synth.WORKLOADS["full"])
+    T = w["n_ctx"]
+    cap = T + 64
     layers = []
     for layer in range(w["n_layers"]):
         inp = synth.attn_inputs(**dict(w, seed=5000 + 100 * layer))
-        t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("k_cache", "v_cache", "q", "k_tree", "v_tree")}
+        t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("q", "k_tree", "v_tree")}
+        for k in ("k_cache", "v_cache"):
+            c = torch.empty((w["n_kv_heads"], cap, inp[k].shape[2]), dtype=torch.uint8, device=dev)
+            c[:, :T] = torch.from_numpy(inp[k]).to(dev)
+            t[k] = c
         ts, hs = tv.cache_strides(t["k_cache"], tv.TV_KV_Q4_0)
         desc, par = tv.make_desc(inp["parent"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"], tv.TV_KV_Q4_0,
-                                 w["n_ctx"], 0, inp["scale"], ts, hs)
+                                 T, 0, inp["scale"], ts, hs)
         wsb = tv.tv_attn_workspace_bytes(desc)
         t["ws"] = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         t["wsb"], t["desc"], t["par"] = wsb, desc, par
+        t["cdesc"] = tv.make_commit_desc(len(inp["parent"]), w["n_kv_heads"], w["head_dim"], tv.TV_KV_Q4_0, T, cap,
+                                         ts, hs)
         t["out"] = torch.empty((len(inp["parent"]), w["n_q_heads"], w["head_dim"]), dtype=torch.float32, device=dev)
         layers.append(t)
     parent = synth.attn_inputs(**dict(w, seed=5000))["parent"]
@@ -273,12 +283,16 @@ def full_step(tv, synth, dev, stream, steps):
     res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
     aws = torch.empty(tv.tv_accept_workspace_bytes(n, w["vocab"]), dtype=torch.uint8, device=dev)
     host = torch.empty(2 + 2 * n, dtype=torch.int32, pin_memory=True)
+    # every layer's cache has the same shape and strides: one commit launch
+    k_trees, v_trees = [t["k_tree"] for t in layers], [t["v_tree"] for t in layers]
+    k_caches, v_caches = [t["k_cache"] for t in layers], [t["v_cache"] for t in layers]
 
     def one_step():
         for t in layers:
             tv.tree_verify_attn(t["desc"], t["k_cache"], t["v_cache"], t["q"], t["k_tree"], t["v_tree"], t["out"],
                                 t["ws"], t["wsb"], stream)
         tv.tree_accept(lg, parent, tokens, am, res, aws, stream)
+        tv.tree_commit_kv_layers(layers[0]["cdesc"], res, k_trees, v_trees, k_caches, v_caches, stream)
 
     for _ in range(3):
         one_step()
@@ -301,7 +315,7 @@ def full_step(tv, synth, dev, stream, steps):
     return {
         "full_step": {
             "workload": "16 layers x (24 q / 4 kv heads, head_dim 256, 32768 Q4_0 rows, budget-22 tree) + acceptance "
-                        "over 23x152000 logits",
+                        "over 23x152000 logits + KV commit of the accepted path into the 16 layers (one launch)",
             "steps_per_s_pipelined": 1e3 / pipelined_ms,
             "ms_per_step_pipelined": pipelined_ms,
             "steps_per_s_with_host_sync": 1e3 / synced_ms,

@@ -16,7 +16,10 @@
  *                     attends to the committed cache rows (inside the window)
  *                     and to its own tree ancestors, itself included;
  *   tree_accept       greedy acceptance: per-node argmax over the vocabulary
- *                     and the longest root path whose draft tokens match.
+ *                     and the longest root path whose draft tokens match;
+ *   tree_commit_kv    the step after acceptance: the accepted path's K/V
+ *                     rows appended to one layer's cache (Q4_0 or F16);
+ *                     tree_commit_kv_layers does every layer in one launch.
  *
  * Conventions shared by all calls
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
@@ -169,6 +172,71 @@ TV_API size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab);
 TV_API int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
                 const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * Shape of one layer's KV commit.
+ *
+ * n_nodes      size of the verified tree, 1..TV_MAX_NODES.
+ * n_kv_heads   KV heads H_kv (>= 1).
+ * head_dim     64, 128 or 256.
+ * kv_type      TV_KV_F16 or TV_KV_Q4_0.
+ * n_ctx        rows committed before this step (>= 0): position r of the
+ *              accepted path (r = 0 is the root) goes to row n_ctx + r.
+ * capacity     rows allocated per KV head; n_ctx + n_nodes <= capacity, so
+ *              every possible path fits.
+ * kv_token_stride, kv_head_stride  as in tv_attn_desc (same rules).
+ */
+typedef struct tv_commit_desc {
+    int32_t n_nodes;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t kv_type;
+    int64_t n_ctx;
+    int64_t capacity;
+    int64_t kv_token_stride;
+    int64_t kv_head_stride;
+} tv_commit_desc;
+
+/*
+ * Appends the accepted path of a verify step to one layer's KV cache,
+ * asynchronous on `stream`. After greedy acceptance the root and the accepted
+ * nodes are committed tokens (Luce DFlash pages: the verify state keeps the
+ * target's cache in Q4_0 or F16); their K and V rows move from the tree
+ * buffers into the cache.
+ *
+ * result      device int32[2 + 2*n_nodes], the result_out of tree_accept for
+ *             the same tree (read on the device: the commit may follow the
+ *             acceptance on the stream without a host round trip). n_acc =
+ *             result[0]; the path is result[2 .. 2 + n_acc].
+ * k_tree, v_tree  device fp16 [n_nodes][n_kv_heads][head_dim], 16-byte
+ *             aligned: the K/V rows the verify pass used for the nodes.
+ * k_cache, v_cache  device caches laid out by the strides, 16-byte aligned.
+ *             For r = 0 .. n_acc, row n_ctx + r of every KV head receives
+ *             node result[2 + r]'s row: copied for F16; for Q4_0 quantised
+ *             per 32-value block with m = the value of largest magnitude
+ *             (the first on ties), scale d = m / -8 stored as fp16 (nearest,
+ *             ties to even), and code = floor(x * (1/d) + 8.5) clamped to
+ *             0..15 (product and sum rounded separately in fp32; a zero
+ *             block gets scale +0 and codes 8; NaN gets code 0). No other row is written.
+ *             A result whose n_acc or path node is out of range writes
+ *             nothing.
+ * Returns TV_OK or a TV_E_* code (nothing is launched on error).
+ */
+TV_API int tree_commit_kv(const tv_commit_desc *d, const int32_t *result, const void *k_tree, const void *v_tree,
+                   void *k_cache, void *v_cache, void *stream);
+
+/*
+ * tree_commit_kv for n_layers layers of the same shape at once (one launch
+ * per 64 layers): k_tree, v_tree, k_cache, v_cache are HOST arrays of
+ * n_layers device pointers, layer l's buffers at index l, each as in
+ * tree_commit_kv; all layers share `d` (so the same strides and n_ctx) and
+ * the acceptance result. The arrays are read during the call only.
+ * Returns TV_OK or a TV_E_* code (nothing is launched on error; every layer's
+ * pointers are checked before the first launch).
+ */
+TV_API int tree_commit_kv_layers(const tv_commit_desc *d, int32_t n_layers, const int32_t *result,
+                          const void *const *k_tree, const void *const *v_tree, void *const *k_cache,
+                          void *const *v_cache, void *stream);
 
 /* Static string for a status code. */
 TV_API const char *tv_strerror(int code);

@@ -124,3 +124,41 @@ def test_library_links_no_oracle():
     for src in os.listdir(tvbuild.CSRC):
         text = open(os.path.join(tvbuild.CSRC, src)).read()
         assert "tvref" not in text and "oracle" not in text.lower(), src
+
+
+def test_commit_argument_checks(L):
+    def call(n=5, hkv=2, D=64, kv=tv.TV_KV_Q4_0, n_ctx=10, cap=20, ts=36, hs=36 * 20, ptrs=(4096,) * 5):
+        d = tv.make_commit_desc(n, hkv, D, kv, n_ctx, cap, ts, hs)
+        return L.tree_commit_kv(ctypes.byref(d), *ptrs, None)
+
+    assert L.tree_commit_kv(None, 4096, 4096, 4096, 4096, 4096, None) == -1
+    assert call(n=0) == -3 and call(n=65) == -3
+    assert call(hkv=0) == -3
+    assert call(D=96) == -3
+    assert call(kv=9) == -1
+    assert call(n_ctx=-1) == -3
+    assert call(n_ctx=16) == -3             # 16 + 5 rows would pass the capacity of 20
+    assert call(ts=35) == -3                # below the Q4_0 row size
+    assert call(ts=38) == -4                # Q4_0 strides: multiples of 4
+    assert call(kv=tv.TV_KV_F16, ts=136, hs=136 * 20) == -4
+    assert call(ptrs=(None, 4096, 4096, 4096, 4096)) == -1
+    assert call(ptrs=(4096, 4096, 4096, 4096, None)) == -1
+    assert call(ptrs=(4098, 4096, 4096, 4096, 4096)) == -4   # result must be 4-byte aligned
+    assert call(ptrs=(4096, 4104, 4096, 4096, 4096)) == -4   # tree rows 16-byte aligned
+    assert call(ptrs=(4096, 4096, 4096, 4100, 4096)) == -4   # caches 16-byte aligned
+
+
+def test_commit_layers_argument_checks(L):
+    d = tv.make_commit_desc(5, 2, 64, tv.TV_KV_Q4_0, 10, 20, 36, 36 * 20)
+    arr = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    ok = arr(4096, 4096, 4096)
+    f = lambda nl, res=4096, kt=ok, vt=ok, kc=ok, vc=ok: L.tree_commit_kv_layers(
+        ctypes.byref(d), nl, res, kt, vt, kc, vc, None)
+    assert f(0) == -3
+    assert f(3, res=None) == -1
+    assert f(3, kt=None) == -1
+    assert f(3, vc=arr(4096, None, 4096)) == -1      # a null pointer in layer 1
+    assert f(3, kc=arr(4096, 4096, 4100)) == -4      # a misaligned cache in layer 2
+    assert f(3, res=4098) == -4
+    bad = tv.make_commit_desc(5, 2, 64, tv.TV_KV_Q4_0, 16, 20, 36, 36 * 20)
+    assert L.tree_commit_kv_layers(ctypes.byref(bad), 3, 4096, ok, ok, ok, ok, None) == -3

@@ -81,12 +81,29 @@ def lib():
         L.tv_accept_workspace_bytes.restype = ctypes.c_size_t
         L.tree_accept.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, ctypes.c_size_t, P]
         L.tree_accept.restype = ctypes.c_int
+        L.tree_commit_kv.argtypes = [ctypes.POINTER(TvCommitDesc), P, P, P, P, P, P]
+        L.tree_commit_kv.restype = ctypes.c_int
+        L.tree_commit_kv_layers.argtypes = [ctypes.POINTER(TvCommitDesc), ctypes.c_int32, P, P, P, P, P, P]
+        L.tree_commit_kv_layers.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
-EXPORTS = ("tree_verify_attn", "tree_accept", "tv_attn_workspace_bytes", "tv_accept_workspace_bytes",
-           "tv_strerror")
+class TvCommitDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_nodes", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_type", ctypes.c_int32),
+        ("n_ctx", ctypes.c_int64),
+        ("capacity", ctypes.c_int64),
+        ("kv_token_stride", ctypes.c_int64),
+        ("kv_head_stride", ctypes.c_int64),
+    ]
+
+
+EXPORTS = ("tree_verify_attn", "tree_accept", "tree_commit_kv", "tree_commit_kv_layers", "tv_attn_workspace_bytes",
+           "tv_accept_workspace_bytes", "tv_strerror")
 
 
 def tv_strerror(code: int) -> str:
@@ -169,3 +186,30 @@ def tree_accept(logits, parent, tokens, argmax_out, result_out, workspace, strea
                            _ptr(workspace), int(wsb), _stream_ptr(stream))
     if rc != TV_OK:
         raise TvError(rc, "tree_accept")
+
+
+def make_commit_desc(n_nodes, n_kv_heads, head_dim, kv_type, n_ctx, capacity, kv_token_stride, kv_head_stride):
+    return TvCommitDesc(int(n_nodes), int(n_kv_heads), int(head_dim), int(kv_type), int(n_ctx), int(capacity),
+                        int(kv_token_stride), int(kv_head_stride))
+
+
+def tree_commit_kv(desc: TvCommitDesc, result, k_tree, v_tree, k_cache, v_cache, stream=None) -> None:
+    """Append the accepted path (tree_accept's device result) to one layer's
+    caches: torch device tensors, caches head-major as for tree_verify_attn."""
+    rc = lib().tree_commit_kv(ctypes.byref(desc), _ptr(result), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
+                              _ptr(v_cache), _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_commit_kv")
+
+
+def tree_commit_kv_layers(desc: TvCommitDesc, result, k_trees, v_trees, k_caches, v_caches, stream=None) -> None:
+    """tree_commit_kv over several layers in one launch: lists of torch device
+    tensors, one entry per layer, all of the shape `desc` describes."""
+    nl = len(k_trees)
+    if not (len(v_trees) == len(k_caches) == len(v_caches) == nl):
+        raise ValueError("one K/V tree row buffer and one K/V cache per layer")
+    arr = lambda ts: (ctypes.c_void_p * nl)(*[int(t.data_ptr()) for t in ts])
+    rc = lib().tree_commit_kv_layers(ctypes.byref(desc), nl, _ptr(result), arr(k_trees), arr(v_trees),
+                                     arr(k_caches), arr(v_caches), _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_commit_kv_layers")

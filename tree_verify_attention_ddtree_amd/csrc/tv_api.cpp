@@ -16,6 +16,8 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
 size_t accept_ws_bytes(int n, int vocab);
 int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
+int launch_commit(const tv_commit_desc *d, int n_layers, const int32_t *result, const void *const *k_tree,
+                  const void *const *v_tree, void *const *k_cache, void *const *v_cache, hipStream_t stream);
 
 // Splits are sized so one launch fills the device with about one workgroup
 // per compute unit, down to one chunk per split: a split's fixed cost (Q
@@ -203,6 +205,56 @@ int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32
     if (!aligned(workspace, 8)) return TV_E_ALIGN;
     return tv::launch_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out, workspace,
                              (hipStream_t)stream);
+}
+
+static int check_commit_desc(const tv_commit_desc *d)
+{
+    if (!d) return TV_E_ARG;
+    if (d->n_nodes < 1 || d->n_nodes > TV_MAX_NODES || d->n_kv_heads < 1) return TV_E_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return TV_E_SHAPE;
+    if (d->kv_type != TV_KV_F16 && d->kv_type != TV_KV_Q4_0) return TV_E_ARG;
+    if (d->n_ctx < 0 || d->capacity < 0 || d->n_ctx > d->capacity - d->n_nodes) return TV_E_SHAPE;
+    const int64_t row = d->kv_type == TV_KV_Q4_0 ? (int64_t)d->head_dim / 32 * 18 : (int64_t)d->head_dim * 2;
+    const int64_t al = d->kv_type == TV_KV_Q4_0 ? 4 : 16;
+    if (d->kv_token_stride < row || d->kv_head_stride < 0) return TV_E_SHAPE;
+    if (d->kv_token_stride % al || d->kv_head_stride % al) return TV_E_ALIGN;
+    return TV_OK;
+}
+
+static int check_commit_layer(const void *k_tree, const void *v_tree, const void *k_cache, const void *v_cache)
+{
+    if (!k_tree || !v_tree || !k_cache || !v_cache) return TV_E_ARG;
+    if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return TV_E_ALIGN;
+    return TV_OK;
+}
+
+int tree_commit_kv(const tv_commit_desc *d, const int32_t *result, const void *k_tree, const void *v_tree,
+                   void *k_cache, void *v_cache, void *stream)
+{
+    int rc = check_commit_desc(d);
+    if (rc) return rc;
+    if (!result) return TV_E_ARG;
+    if (!aligned(result, 4)) return TV_E_ALIGN;
+    rc = check_commit_layer(k_tree, v_tree, k_cache, v_cache);
+    if (rc) return rc;
+    return tv::launch_commit(d, 1, result, &k_tree, &v_tree, &k_cache, &v_cache, (hipStream_t)stream);
+}
+
+int tree_commit_kv_layers(const tv_commit_desc *d, int32_t n_layers, const int32_t *result,
+                          const void *const *k_tree, const void *const *v_tree, void *const *k_cache,
+                          void *const *v_cache, void *stream)
+{
+    int rc = check_commit_desc(d);
+    if (rc) return rc;
+    if (n_layers < 1) return TV_E_SHAPE;
+    if (!result || !k_tree || !v_tree || !k_cache || !v_cache) return TV_E_ARG;
+    if (!aligned(result, 4)) return TV_E_ALIGN;
+    for (int l = 0; l < n_layers; ++l) {
+        rc = check_commit_layer(k_tree[l], v_tree[l], k_cache[l], v_cache[l]);
+        if (rc) return rc;
+    }
+    return tv::launch_commit(d, n_layers, result, k_tree, v_tree, k_cache, v_cache, (hipStream_t)stream);
 }
 
 }  // extern "C"
