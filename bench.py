@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=552, help="oracle output rows timed for the CPU baseline")
     ap.add_argument("--no-full-step", action="store_true", help="skip the 16-layer verify-step measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="attention cost against tree size (1..64 nodes), context and KV type; one JSON line per "
+                         "point, then a markdown table")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only copy a device buffer of this many bytes --steps times (HBM counter calibration)")
     return ap.parse_args()
@@ -105,6 +108,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.sweep:
+        budget_sweep(args)
         return
 
     import torch
@@ -323,6 +329,82 @@ def full_step(tv, synth, dev, stream, steps):
             "kv_gbps": 16 * 2 * 4 * 32768 * 144 / (pipelined_ms * 1e-3) / 1e9,
         }
     }
+
+
+def budget_sweep(args):
+    """Attention launch time against the tree size n (1..64 nodes) at 8K, 32K
+    and 128K context, Q4_0 and F16, with the 27B head layout (24 q / 4 kv
+    heads, head_dim 256): random draft trees of depth <= 16, plus chains of
+    the same size. The cache rotates over copies spanning >= 1.1 GB so that
+    every launch streams it from HBM. Each point: the average of 200 launches
+    after 50, the KV bandwidth, the MFMA rate and the fraction of the binding
+    roofline (HBM below 312 FLOP per KV byte, MFMA above)."""
+    import torch
+
+    import synth
+    import tree_verify_attention_ddtree_amd as tv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    Hq, Hkv, D = 24, 4, 256
+    sizes = [1, 2, 4, 8, 12, 16, 23, 32, 48, 64]
+    rows = []
+    for kv in ("q4_0", "f16"):
+        for T in (8192, 32768, 131072):
+            inp = synth.attn_inputs(Hq, Hkv, D, T, 64, 16, seed=900 + T, kv=kv)
+            kc0 = torch.from_numpy(inp["k_cache"]).to(dev)
+            vc0 = torch.from_numpy(inp["v_cache"]).to(dev)
+            layer_bytes = 2 * kc0.numel() * kc0.element_size()
+            ncp = max(1, int(np.ceil(1.1e9 / layer_bytes)))
+            caches = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(ncp - 1)]
+            kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+            ts, hs = tv.cache_strides(kc0, kvt)
+            rng = np.random.default_rng(T)
+            for n in sizes:
+                for shape in ("tree", "chain"):
+                    if shape == "chain" and n not in (16, 23, 64):
+                        continue
+                    parent = synth.chain_tree(n) if shape == "chain" else synth.draft_tree(rng, n, 16)
+                    q = torch.from_numpy(np.ascontiguousarray(inp["q"][:n])).to(dev)
+                    kt = torch.from_numpy(np.ascontiguousarray(inp["k_tree"][:n])).to(dev)
+                    vt = torch.from_numpy(np.ascontiguousarray(inp["v_tree"][:n])).to(dev)
+                    out = torch.empty((n, Hq, D), dtype=torch.float32, device=dev)
+                    desc, _par = tv.make_desc(parent, Hq, Hkv, D, kvt, T, 0, inp["scale"], ts, hs)
+                    wsb = tv.tv_attn_workspace_bytes(desc)
+                    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+                    def launch(i):
+                        kc, vc = caches[i % ncp]
+                        tv.tree_verify_attn(desc, kc, vc, q, kt, vt, out, ws, wsb, stream)
+
+                    for i in range(50):
+                        launch(i)
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for i in range(200):
+                        launch(i)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) / 200 * 1e3
+                    flops = 4.0 * Hq * n * T * D
+                    kvb = layer_bytes
+                    gbps = kvb / (us * 1e-6) / 1e9
+                    tfl = flops / (us * 1e-6) / 1e12
+                    mfma_bound = flops / kvb > MFMA_FP16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+                    frac = tfl / MFMA_FP16_PEAK_TFLOPS if mfma_bound else gbps / HBM_PEAK_GBPS
+                    row = dict(kv=kv, n_ctx=T, n=n, tree=shape, us=us, kv_gbps=gbps, tflops=tfl,
+                               bound="mfma" if mfma_bound else "hbm", frac=frac)
+                    rows.append(row)
+                    print(json.dumps(row), flush=True)
+            del caches, kc0, vc0
+            torch.cuda.empty_cache()
+    print("| KV | ctx | n | tree | us | KV GB/s | TFLOP/s | bound | frac |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['kv']} | {r['n_ctx']} | {r['n']} | {r['tree']} | {r['us']:.1f} | {r['kv_gbps']:.0f} | "
+              f"{r['tflops']:.0f} | {r['bound']} | {r['frac']:.3f} |")
 
 
 def cpu_baseline(inp, logits, parent, tokens, n_rows):
