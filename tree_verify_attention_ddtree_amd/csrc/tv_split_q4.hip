@@ -355,7 +355,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 
         // ---- S^T = K Q^T for every slot and the 4 key tiles of the chunk,
         // with the K dequantisation of chunk c+1 in between. K fragments
-        // stream through a 3-entry ring, two ahead of use.
+        // stream through a 4-entry ring, three ahead of use (an LDS read under
+        // load takes longer than the 2 x 3 MFMAs a two-ahead ring covers).
         constexpr int TOT = NB * 4;
         f4 sacc[NS][4];
 #pragma unroll
@@ -366,16 +367,17 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
             const int bb = i / 4, kt = i % 4;
             return *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
         };
-        h8 kr[3];
+        h8 kr[4];
         kr[0] = kfrag(0);
         kr[1] = kfrag(1);
+        kr[2] = kfrag(2);
 #pragma unroll
         for (int i = 0; i < TOT; ++i) {
-            if (i + 2 < TOT) kr[(i + 2) % 3] = kfrag(i + 2);
+            if (i + 3 < TOT) kr[(i + 3) % 4] = kfrag(i + 3);
             const int bb = i / 4, kt = i % 4;
 #pragma unroll
             for (int k = 0; k < NS; ++k)
-                sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[i % 3], qf[k][bb], sacc[k][kt], 0, 0, 0);
+                sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[i % 4], qf[k][bb], sacc[k][kt], 0, 0, 0);
             if (kt == 3) {
                 ld.k_piece(bb, ks_n, magic);
                 TV_SCHED_FENCE();
@@ -449,20 +451,21 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         };
         constexpr int VP = L::V_PIECES;
         constexpr int VSTEP = NDT / VP;
-        h8 vr[3];
+        h8 vr[4];
         vr[0] = vfrag(0);
         vr[1] = vfrag(1);
+        vr[2] = vfrag(2);
 #pragma unroll
         for (int i = 0; i < TV; ++i) {
-            if (i + 2 < TV) vr[(i + 2) % 3] = vfrag(i + 2);
+            if (i + 3 < TV) vr[(i + 3) % 4] = vfrag(i + 3);
             const int kk = i / NDT, j = i % NDT;
 #pragma unroll
             for (int k = 0; k < NOWN; ++k)
-                o[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 3], pf[k][kk], o[k][j], 0, 0, 0);
+                o[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 4], pf[k][kk], o[k][j], 0, 0, 0);
             if (j < NDQ) {
 #pragma unroll
                 for (int u = 0; u < NSH; ++u)
-                    osh[u][j < NDQ ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 3], pf[NOWN + u][kk],
+                    osh[u][j < NDQ ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 4], pf[NOWN + u][kk],
                                                                                    osh[u][j < NDQ ? j : 0], 0, 0, 0);
             }
             if (i == 1) {
