@@ -56,7 +56,7 @@ def lib():
         L.tvref_check_tree.restype = i32
         L.tvref_ancestors.argtypes = [i32, P, P]
         L.tvref_ancestors.restype = i32
-        L.tvref_attn.argtypes = [i32, P, i32, i32, i32, i64, i64, dbl, i32, P, P, i64, i64, P, P, P, P, i32, P]
+        L.tvref_attn.argtypes = [i32, P, i32, i32, i32, i64, i64, i32, dbl, i32, P, P, i64, i64, P, P, P, P, i32, P]
         L.tvref_attn.restype = i32
         L.tvref_argmax_row.argtypes = [P, i32]
         L.tvref_argmax_row.restype = i32
@@ -109,7 +109,8 @@ def check_tree(parent) -> int:
 def attn(inp: dict, rows=None, n_ctx=None) -> np.ndarray:
     """Oracle attention for one layer.
 
-    ``inp`` holds the arrays of ``synth.attn_inputs`` (head-major caches).
+    ``inp`` holds the arrays of ``synth.attn_inputs`` (head-major caches);
+    ``inp["window_mode"]`` (default 0) selects the per-position window (1).
     ``rows``: optional iterable of output rows r = i*H_q + h; other rows of the
     result are NaN. ``n_ctx`` overrides the number of committed rows used.
     Returns float64 [n, H_q, D].
@@ -132,7 +133,8 @@ def attn(inp: dict, rows=None, n_ctx=None) -> np.ndarray:
     vt = np.ascontiguousarray(inp["v_tree"], np.float16)
     out = np.full((n, Hq, D), np.nan, np.float64)
     rws = None if rows is None else np.ascontiguousarray(list(rows), np.int32)
-    rc = lib().tvref_attn(n, _ptr(parent), Hq, Hkv, D, ctx, int(inp.get("window", 0)), float(inp["scale"]), kv,
+    rc = lib().tvref_attn(n, _ptr(parent), Hq, Hkv, D, ctx, int(inp.get("window", 0)),
+                          int(inp.get("window_mode", 0)), float(inp["scale"]), kv,
                           _ptr(kc), _ptr(vc), tok_stride, head_stride, _ptr(q.view(np.uint16)),
                           _ptr(kt.view(np.uint16)), _ptr(vt.view(np.uint16)), _ptr(rws),
                           0 if rws is None else len(rws), _ptr(out))

@@ -25,6 +25,11 @@
  *     scale * (code - 8).
  *   - Window W > 0: every node sees cache rows [max(0, n_ctx - W), n_ctx);
  *     W = 0 means all rows. Tree nodes never count against the window.
+ *     Per-position window (window_mode 1): a node at depth k (position
+ *     n_ctx + k) sees the positions [n_ctx + k - W, n_ctx + k] of its own
+ *     sequence: cache rows [max(0, n_ctx + k - W), n_ctx) and the ancestors
+ *     at depth >= k - W, the W + 1 keys a token at that position has in
+ *     token-by-token decoding with the same window.
  *   - GQA: query head h reads KV head h / (H_q / H_kv).
  *   - argmax order: IEEE compare with -0 == +0, NaN below every number, ties
  *     to the smallest index, an all-NaN row gives index 0.
@@ -139,20 +144,22 @@ static void load_cache_row(int kv_type, const uint8_t *base, int64_t tok_stride,
  *   out     double [n][H_q][D]; rows not listed are left untouched
  *
  * For node i and head h (KV head g = h / (H_q/H_kv)) the keys are the cache
- * rows s0..n_ctx-1 in order, then anc(i) in increasing index order;
+ * rows s0..n_ctx-1 in order (s0 per the window and window_mode above), then
+ * anc(i) in increasing index order;
  *   s_j = scale * sum_d q[d] K_j[d]      (d ascending)
  *   m = max_j s_j,  w_j = exp(s_j - m),  l = sum_j w_j   (j ascending)
  *   out[d] = (sum_j w_j V_j[d]) / l      (j ascending)
  */
 int tvref_attn(int n, const int32_t *parent, int H_q, int H_kv, int D, int64_t n_ctx, int64_t window,
-               double scale, int kv_type, const void *k_cache, const void *v_cache, int64_t tok_stride,
-               int64_t head_stride, const uint16_t *q, const uint16_t *k_tree, const uint16_t *v_tree,
-               const int32_t *rows, int n_rows, double *out)
+               int window_mode, double scale, int kv_type, const void *k_cache, const void *v_cache,
+               int64_t tok_stride, int64_t head_stride, const uint16_t *q, const uint16_t *k_tree,
+               const uint16_t *v_tree, const int32_t *rows, int n_rows, double *out)
 {
     int rc = tvref_check_tree(n, parent);
     if (rc) return rc;
     if (H_q < 1 || H_kv < 1 || H_q % H_kv || D < 32 || D % 32 || n_ctx < 0 || window < 0) return TVREF_ESHAPE;
     if (kv_type != TVREF_KV_F16 && kv_type != TVREF_KV_Q4_0) return TVREF_EARG;
+    if (window_mode != 0 && window_mode != 1) return TVREF_EARG;
     if (n_ctx > 0 && (!k_cache || !v_cache)) return TVREF_EARG;
     const int G = H_q / H_kv;
     const int64_t s0 = (window > 0 && n_ctx > window) ? n_ctx - window : 0;
@@ -174,16 +181,27 @@ int tvref_attn(int n, const int32_t *parent, int H_q, int H_kv, int D, int64_t n
             const int r = rows ? rows[t] : t;
             const int i = r / H_q, h = r % H_q, g = h / G;
             const int na = tvref_ancestors(i, parent, anc);
+            /* per-position window: the node's depth k = na - 1 moves its
+             * start to n_ctx + k - W, in the cache and along its path (anc[a]
+             * is at depth a) */
+            int64_t si = s0;
+            int a0 = 0;
+            if (window_mode == 1 && window > 0) {
+                si = n_ctx + (na - 1) - window;
+                if (si < 0) si = 0;
+                const int64_t first = (int64_t)(na - 1) - window;
+                a0 = first > 0 ? (int)first : 0;
+            }
             half_row(q + ((int64_t)i * H_q + h) * D, D, qd);
             /* pass 1: scores */
             int64_t nk = 0;
-            for (int64_t j = s0; j < n_ctx; ++j) {
+            for (int64_t j = si; j < n_ctx; ++j) {
                 load_cache_row(kv_type, (const uint8_t *)k_cache, tok_stride, head_stride, g, j, D, K);
                 double s = 0.0;
                 for (int d = 0; d < D; ++d) s += qd[d] * K[d];
                 sc[nk++] = scale * s;
             }
-            for (int a = 0; a < na; ++a) {
+            for (int a = a0; a < na; ++a) {
                 half_row(k_tree + ((int64_t)anc[a] * H_kv + g) * D, D, K);
                 double s = 0.0;
                 for (int d = 0; d < D; ++d) s += qd[d] * K[d];
@@ -195,13 +213,13 @@ int tvref_attn(int n, const int32_t *parent, int H_q, int H_kv, int D, int64_t n
             double l = 0.0;
             for (int d = 0; d < D; ++d) acc[d] = 0.0;
             nk = 0;
-            for (int64_t j = s0; j < n_ctx; ++j) {
+            for (int64_t j = si; j < n_ctx; ++j) {
                 const double w = exp(sc[nk++] - m);
                 l += w;
                 load_cache_row(kv_type, (const uint8_t *)v_cache, tok_stride, head_stride, g, j, D, K);
                 for (int d = 0; d < D; ++d) acc[d] += w * K[d];
             }
-            for (int a = 0; a < na; ++a) {
+            for (int a = a0; a < na; ++a) {
                 const double w = exp(sc[nk++] - m);
                 l += w;
                 half_row(v_tree + ((int64_t)anc[a] * H_kv + g) * D, D, K);
