@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="long", choices=["long", "27b", "window"])
     ap.add_argument("--kv", default="q4_0", choices=["q4_0", "f16"])
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9, help="KV bytes the copies span at least")
+    ap.add_argument("--window-mode", type=int, default=0, choices=[0, 1],
+                    help="1: per-position sliding window (a node at depth k sees positions [n_ctx+k-W, n_ctx+k])")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=552, help="oracle output rows timed for the CPU baseline")
     ap.add_argument("--no-full-step", action="store_true", help="skip the 16-layer verify-step measurement")
@@ -143,7 +145,7 @@ def main():
     vt = torch.from_numpy(inp["v_tree"]).to(dev)
     out = torch.empty((n, Hq, D), dtype=torch.float32, device=dev)
     ts, hs = tv.cache_strides(kc0, kvt)
-    desc, _par = tv.make_desc(parent, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs)
+    desc, _par = tv.make_desc(parent, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs, window_mode=args.window_mode)
     wsb = tv.tv_attn_workspace_bytes(desc)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     lg = torch.from_numpy(logits).to(dev)
@@ -154,7 +156,7 @@ def main():
 
     # chain-16 comparison (same cache, block-size-16 chain instead of the tree)
     chain = synth.chain_tree(16)
-    cdesc, _cpar = tv.make_desc(chain, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs)
+    cdesc, _cpar = tv.make_desc(chain, Hq, Hkv, D, kvt, T, W, inp["scale"], ts, hs, window_mode=args.window_mode)
     cws = torch.empty(max(tv.tv_attn_workspace_bytes(cdesc), 16), dtype=torch.uint8, device=dev)
     cq, ckt, cvt = q[:16].contiguous(), kt[:16].contiguous(), vt[:16].contiguous()
     cout = torch.empty((16, Hq, D), dtype=torch.float32, device=dev)
@@ -219,7 +221,7 @@ def main():
             "workload": (f"one verify step: tree-verify attention (1 layer, {Hq} q / {Hkv} kv heads, head_dim {D}, "
                          f"ctx {T}, window {W}, {args.kv} KV, budget-22 tree of {n} nodes) + greedy acceptance "
                          f"over {n}x{vocab} fp32 logits"),
-            "kv": args.kv, "n_ctx": T, "window": W, "n_nodes": n, "vocab": vocab,
+            "kv": args.kv, "n_ctx": T, "window": W, "window_mode": args.window_mode, "n_nodes": n, "vocab": vocab,
             "kv_copies_rotated": n_copies,
         },
         "kv_gbps": kv_gbps,

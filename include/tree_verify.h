@@ -78,6 +78,12 @@ extern "C" {
  * window       0: attend to all rows; W > 0: only to rows
  *              [max(0, n_ctx - W), n_ctx). The window counts cache rows only;
  *              every node also sees all of its ancestors.
+ * window_mode  0: the window above, the same for every node. 1: per
+ *              position: a node at depth k (position n_ctx + k) sees the
+ *              positions [n_ctx + k - W, n_ctx + k] of its own sequence, i.e.
+ *              cache rows [max(0, n_ctx + k - W), n_ctx) and its ancestors at
+ *              depth >= k - W: the keys that position has in token-by-token
+ *              decoding with window W. No effect when window == 0.
  * kv_token_stride  bytes from row j to row j+1 of one KV head (>= row size,
  *              multiple of 4 for Q4_0 and of 16 for F16).
  * kv_head_stride   bytes from KV head g to g+1 (multiple of 4 / 16 likewise).
@@ -98,6 +104,7 @@ typedef struct tv_attn_desc {
     int64_t kv_token_stride;
     int64_t kv_head_stride;
     float scale;
+    int32_t window_mode;
 } tv_attn_desc;
 
 /*

@@ -31,7 +31,7 @@ def gpu_attn(inp, dev="cuda", n_ctx=None, window=None, tensors=None, strides=Non
     ctx = inp["k_cache"].shape[1] if n_ctx is None else n_ctx
     W = inp.get("window", 0) if window is None else window
     desc, _par = tv.make_desc(inp["parent"], inp["n_q_heads"], inp["n_kv_heads"], inp["head_dim"], kv, ctx, W,
-                              inp["scale"], ts, hs)
+                              inp["scale"], ts, hs, window_mode=inp.get("window_mode", 0))
     wsb = tv.tv_attn_workspace_bytes(desc)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     n = len(inp["parent"])

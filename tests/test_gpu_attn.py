@@ -208,3 +208,30 @@ def test_deterministic():
     inp = synth.attn_inputs(**synth.WORKLOADS["27b"])
     a, b = gpu_attn(inp, repeat=2)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+@pytest.mark.parametrize("W,n_ctx", [(1, 700), (5, 700), (12, 700), (63, 700), (64, 700), (65, 700), (100, 4097),
+                                     (2047, 4097), (2048, 4097), (5000, 4097), (30, 40), (3, 10), (64, 64)])
+def test_per_position_window(kv, W, n_ctx):
+    """window_mode 1: a node at depth k sees positions [n_ctx + k - W, n_ctx + k];
+    windows narrower than the tree's depth, around the 64-row head the merge
+    kernel scores, wider than the context, and contexts shorter than a chunk."""
+    inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=n_ctx, n_nodes=23, depth_cap=16,
+                            seed=4000 + W, kv=kv)
+    inp = dict(inp, window=W, window_mode=1)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_per_position_window_61k_and_deep_chain():
+    w = dict(synth.WORKLOADS["window"])
+    inp = dict(synth.attn_inputs(**w), window_mode=1)
+    rows = sample_rows(23, 24, 24, 7)
+    err = check_rows(gpu_attn(inp), oracle.attn(inp, rows=rows), rows, 24)
+    assert err <= TOL, err
+    # a 64-node chain with a window of 10: ancestors beyond the window drop out
+    ch = dict(synth.attn_inputs(n_q_heads=8, n_kv_heads=2, head_dim=128, n_ctx=300, n_nodes=64, depth_cap=64,
+                                seed=77, kv="q4_0", parent=synth.chain_tree(64)), window=10, window_mode=1)
+    err = rownorm_err(gpu_attn(ch).astype(np.float64), oracle.attn(ch))
+    assert err <= TOL, err

@@ -162,3 +162,11 @@ def test_commit_layers_argument_checks(L):
     assert f(3, res=4098) == -4
     bad = tv.make_commit_desc(5, 2, 64, tv.TV_KV_Q4_0, 16, 20, 36, 36 * 20)
     assert L.tree_commit_kv_layers(ctypes.byref(bad), 3, 4096, ok, ok, ok, ok, None) == -3
+
+
+def test_window_mode_checked(L):
+    d, keep = _desc()
+    d.window_mode = 2
+    assert _call(L, d) == -1
+    d.window_mode = 1
+    assert _call(L, d) not in (-1, -3, -4)  # valid: fails only later, on the device

@@ -39,6 +39,7 @@ class TvAttnDesc(ctypes.Structure):
         ("kv_token_stride", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64),
         ("scale", ctypes.c_float),
+        ("window_mode", ctypes.c_int32),
     ]
 
 
@@ -126,13 +127,13 @@ def _stream_ptr(stream):
 
 
 def make_desc(parent, n_q_heads, n_kv_heads, head_dim, kv_type, n_ctx, window, scale, kv_token_stride=0,
-              kv_head_stride=0):
+              kv_head_stride=0, window_mode=0):
     """A TvAttnDesc plus the int32 buffer its parent pointer refers to (keep
     both alive while the descriptor is used)."""
     par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
     d = TvAttnDesc(len(par), par.ctypes.data_as(ctypes.c_void_p).value, int(n_q_heads), int(n_kv_heads),
                    int(head_dim), int(kv_type), int(n_ctx), int(window), int(kv_token_stride),
-                   int(kv_head_stride), float(scale))
+                   int(kv_head_stride), float(scale), int(window_mode))
     return d, par
 
 

@@ -44,6 +44,7 @@ static int check_desc(const tv_attn_desc *d)
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return TV_E_SHAPE;
     if (d->kv_type != TV_KV_F16 && d->kv_type != TV_KV_Q4_0) return TV_E_ARG;
     if (d->n_ctx < 0 || d->window < 0) return TV_E_SHAPE;
+    if (d->window_mode != 0 && d->window_mode != 1) return TV_E_ARG;
     if (!(d->scale > 0.0f) || !isfinite(d->scale)) return TV_E_ARG;
     if ((int64_t)d->n_nodes * d->n_q_heads > (int64_t)1 << 24) return TV_E_SHAPE;
     if (d->n_ctx > 0) {
@@ -88,9 +89,23 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     if (rc) return rc;
     out->s0 = (d->window > 0 && d->n_ctx > d->window) ? d->n_ctx - d->window : 0;
     out->R = d->n_ctx - out->s0;
-    // whole chunks go to the split kernel; the last R % kChunk rows of the
-    // window are attended by the merge kernel together with the tree
-    out->n_chunks = out->R / kChunk;
+    // per-position window: the first rows of the window, where the nodes'
+    // windows start at different rows (a node at depth k starts k rows after
+    // a root, so they span the tree's depth), go to the merge kernel, which
+    // scores them per node
+    out->head = 0;
+    if (d->window_mode == 1 && d->window > 0) {
+        int depth[TV_MAX_NODES], max_depth = 0;
+        depth[0] = 0;
+        for (int i = 1; i < d->n_nodes; ++i) {
+            depth[i] = depth[d->parent[i]] + 1;
+            max_depth = depth[i] > max_depth ? depth[i] : max_depth;
+        }
+        out->head = out->R < max_depth ? out->R : max_depth;
+    }
+    // whole chunks of the rest go to the split kernel; its last
+    // (R - head) % kChunk rows are attended by the merge kernel with the tree
+    out->n_chunks = (out->R - out->head) / kChunk;
     if (out->n_chunks == 0) {
         out->S = 0;
         return TV_OK;

@@ -421,6 +421,11 @@ struct MergeArgs {
     int32_t G;
     int32_t S;
     float c;  // scale * log2(e)
+    // per-position window: cache rows [head_begin, head_begin + n_head) are
+    // scored here, node i skipping the first head_skip[i] of them
+    int64_t head_begin;
+    int32_t n_head;
+    uint8_t head_skip[TV_MAX_NODES];
     // cache rows [tail_begin, tail_end) of the window that do not fill a
     // whole chunk of the split kernel
     const uint8_t *k_cache;
@@ -480,7 +485,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     constexpr int SMAX = 8;         // splits per thread held in registers
     constexpr int VPF = 2;          // extra keys per split group whose V is loaded early
     static_assert(32 % KPT == 0, "a lane's key slice lies inside one 32-value block");
-    __shared__ float sk[TV_MAX_NODES + kChunk];
+    __shared__ float sk[TV_MAX_NODES + 2 * kChunk];
     __shared__ float red_s[NGR];
     __shared__ float red_k[4];
     __shared__ __attribute__((aligned(16))) float acc_s[NGR][D];
@@ -491,7 +496,13 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     const int i = row / a.H_q, h = row % a.H_q, g = h / a.G;
     const uint64_t anc = a.anc[i];
     const int na = __builtin_popcountll(anc);
-    const int nk = na + a.n_tail;
+    const int hs = a.head_skip[i];
+    const int nh = a.n_head - hs;     // head rows this node sees
+    const int nk = na + nh + a.n_tail;
+    // extra key kk -> cache row (head rows, then tail rows) for kk >= na
+    auto extra_row = [&](int kk) -> int64_t {
+        return kk < na + nh ? a.head_begin + hs + (kk - na) : a.tail_begin + (kk - na - nh);
+    };
     const uint8_t *kh = a.k_cache + (int64_t)g * a.head_stride;
     const uint8_t *vh = a.v_cache + (int64_t)g * a.head_stride;
 
@@ -507,7 +518,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 #pragma unroll
             for (int p = 0; p < 8; ++p) vv[p] = (float)vr[p];
         } else {
-            cache_values<8>(vh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, 8 * dq, vv);
+            cache_values<8>(vh + extra_row(kk) * a.tok_stride, a.kv_type, 8 * dq, vv);
         }
     };
     float vpf[VPF][8];
@@ -571,7 +582,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 #pragma unroll
                     for (int p = 0; p < KPT; ++p) kv[p] = (float)kr[p];
                 } else {
-                    cache_values<KPT>(kh + (a.tail_begin + (kk - na)) * a.tok_stride, a.kv_type, kl * KPT, kv);
+                    cache_values<KPT>(kh + extra_row(kk) * a.tok_stride, a.kv_type, kl * KPT, kv);
                 }
 #pragma unroll
                 for (int p = 0; p < KPT; ++p) part = __builtin_fmaf(qv[p], kv[p], part);
@@ -680,7 +691,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         a.q = (const _Float16 *)p->q;
         a.ws_o = ws_o;
         a.ws_m = ws_m;
-        a.s0 = plan.s0;
+        a.s0 = plan.s0 + plan.head;
         a.key_end = plan.s0 + plan.R;
         a.n_chunks = plan.n_chunks;
         a.NR = NR;
@@ -713,13 +724,36 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
     mg.v_cache = (const uint8_t *)p->v_cache;
     mg.tok_stride = d->kv_token_stride;
     mg.head_stride = d->kv_head_stride;
-    mg.tail_begin = plan.s0 + plan.n_chunks * kChunk;
-    mg.n_tail = (int32_t)(plan.R - plan.n_chunks * kChunk);
+    mg.head_begin = plan.s0;
+    mg.n_head = (int32_t)plan.head;
+    mg.tail_begin = plan.s0 + plan.head + plan.n_chunks * kChunk;
+    mg.n_tail = (int32_t)(plan.R - plan.head - plan.n_chunks * kChunk);
     mg.kv_type = d->kv_type;
-    for (int i = 0; i < TV_MAX_NODES; ++i) mg.anc[i] = 0;
+    for (int i = 0; i < TV_MAX_NODES; ++i) {
+        mg.anc[i] = 0;
+        mg.head_skip[i] = 0;
+    }
     for (int i = 0; i < n; ++i) {
         uint64_t mk = 0;
-        for (int u = i; u >= 0; u = d->parent[u]) mk |= 1ull << u;
+        int depth = -1;
+        for (int u = i; u >= 0; u = d->parent[u]) {
+            mk |= 1ull << u;
+            ++depth;
+        }
+        if (plan.head > 0) {
+            // per-position window: the node at depth k sees positions from
+            // n_ctx + k - W on, in the cache and along its path
+            const int64_t start = d->n_ctx + depth - d->window;
+            int64_t skip = start - plan.s0;
+            skip = skip < 0 ? 0 : (skip > plan.head ? plan.head : skip);
+            mg.head_skip[i] = (uint8_t)skip;
+            const int64_t first = (int64_t)depth - d->window;  // shallowest ancestor depth kept
+            if (first > 0) {
+                int du = depth;
+                for (int u = i; u >= 0; u = d->parent[u], --du)
+                    if (du < first) mk &= ~(1ull << u);
+            }
+        }
         mg.anc[i] = mk;
     }
     dim3 mgrid(NR);

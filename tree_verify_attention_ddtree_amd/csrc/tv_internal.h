@@ -41,7 +41,8 @@ struct SplitPlan {
     RowPlan rows;
     int64_t s0;       // first cache row in the window
     int64_t R;        // cache rows in the window
-    int64_t n_chunks; // whole chunks of the window: R / kChunk
+    int64_t head;     // rows [s0, s0 + head) scored per node by the merge kernel (<= tree depth)
+    int64_t n_chunks; // whole chunks of the rest: (R - head) / kChunk
     int S;            // key-range splits per (KV head, row group)
 };
 
