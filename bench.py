@@ -194,6 +194,7 @@ def main():
                                                    ckt, cvt, cout, cws, None, stream), args.steps)
     assert int(res[0].item()) == planted_L
 
+
     # algorithmic work of one attention launch
     R = T - max(0, T - W) if W > 0 else T
     row_bytes = (D // 32 * 18) if args.kv == "q4_0" else 2 * D
