@@ -218,10 +218,20 @@ split_kernel(const SplitArgs a)
 #pragma unroll
     for (int u = 0; u < NSH; ++u) tile[NOWN + u] = tm.t0 + 4 * NOWN + u;
 
-    h8 qf[NS][NB];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) load_q_frags<D, KVT>(a, gkv, tile[k], t_end, col, grp, qf[k]);
+    const int64_t c_begin = split_chunk_begin(a, split);
+    const int64_t c_end = split_chunk_begin(a, split + 1);
 
+    // the query rows (from L2) are requested first, the first chunk's cache
+    // rows (from HBM) next, so that the two are in flight together and the
+    // query rows can be staged before the cache rows arrive
+    QStage<D, KVT, NOWN, NSH> qs;
+    qs.load(a, gkv, tm.t0, tid);
+    // (every split has at least one chunk: the plan keeps S <= n_chunks)
+    u32 raw[St::RAW];
+    load_raw<D, KVT>(a, gkv, a.s0 + c_begin * kChunk, tid, raw);
+
+    h8 qf[NS][NB];
+    qs.store(tm.t0, tile, tid, col, grp, lds, qf);
     // The Q fragments are read only as MFMA B operands, which may come from
     // AGPRs; parking them there leaves the VGPRs to the accumulators.
 #pragma unroll
@@ -238,12 +248,6 @@ split_kernel(const SplitArgs a)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[k][dt] = (f4){0.f, 0.f, 0.f, 0.f};
     }
-
-    const int64_t c_begin = a.n_chunks * split / a.S;
-    const int64_t c_end = a.n_chunks * (split + 1) / a.S;
-
-    u32 raw[St::RAW];
-    if (c_begin < c_end) load_raw<D, KVT>(a, gkv, a.s0 + c_begin * kChunk, tid, raw);
 
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int st = (int)((c - c_begin) & 1);
@@ -693,7 +697,8 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         a.ws_m = ws_m;
         a.s0 = plan.s0 + plan.head;
         a.key_end = plan.s0 + plan.R;
-        a.n_chunks = plan.n_chunks;
+        a.c_per = plan.n_chunks / plan.S;
+        a.c_rem = (int32_t)(plan.n_chunks % plan.S);
         a.NR = NR;
         a.H_q = Hq;
         a.G = G;

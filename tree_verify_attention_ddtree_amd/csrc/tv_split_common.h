@@ -12,6 +12,20 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32;
+typedef u32 u2v __attribute__((ext_vector_type(2)));
+typedef u32 u3v __attribute__((ext_vector_type(3)));
+typedef u32 u4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes from `base`: loads at an offset
+// past the end return zero and stores there are dropped (the range check
+// covers the per-lane offset plus the immediate).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, u32 bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// a per-lane buffer offset that is always out of range
+constexpr u32 kOffNone = 0x80000000u;
 
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
 // loop to its top, which would need a register per fragment.
@@ -34,14 +48,23 @@ struct SplitArgs {
     float *ws_m;     // [S][NR] log2 of the partial's softmax denominator
     int64_t s0;
     int64_t key_end;  // end of the rows covered by whole chunks
-    int64_t n_chunks;
-    int32_t NR;  // n * H_q
+    int64_t c_per;  // whole chunks per split: n_chunks / S
+    int32_t c_rem;  // n_chunks % S
+    int32_t NR;     // n * H_q
     int32_t H_q;
     int32_t G;
     int32_t M;  // G * n
     int32_t S;
     float c;  // scale * log2(e)
 };
+
+// First chunk of split s (s = S gives n_chunks): floor(n_chunks * s / S),
+// written as s * c_per + floor(s * c_rem / S) so that it needs no 64-bit
+// division (s * c_rem < S * S fits 32 bits for S < 65536).
+__device__ __forceinline__ int64_t split_chunk_begin(const SplitArgs &a, int s)
+{
+    return (int64_t)s * a.c_per + (int64_t)((uint32_t)s * (uint32_t)a.c_rem / (uint32_t)a.S);
+}
 
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 
@@ -169,36 +192,122 @@ struct TileMap {
     }
 };
 
-// Q fragments of one tile (B operand of S^T = K Q^T): lane (col, grp) holds
-// query row 16*tile + col, 8 values per 32-wide block. For Q4_0 the 8 values
-// follow the element order of q4_unpack, for F16 the natural order. Zero for
-// padding rows.
-template <int D, int KVT>
-__device__ __forceinline__ void load_q_frags(const SplitArgs &a, int gkv, int tile, int t_end, int col, int grp,
-                                             h8 (&qf)[D / 32])
-{
-    const int r = 16 * tile + col;
-    if (tile < t_end && r < a.M) {
-        const int node = r / a.G, h = gkv * a.G + r % a.G;
-        const _Float16 *qr = a.q + ((int64_t)node * a.H_q + h) * D;
+// Q fragments of a workgroup's tiles (B operands of S^T = K Q^T), staged
+// through LDS before the first chunk is dequantised there: lane (col, grp)
+// of tile t ends up with query row 16*t + col, 8 values per 32-wide block.
+// For Q4_0 the 8 values follow the element order of q4_unpack, for F16 the
+// natural order.
+//
+// The workgroup reads its rows as contiguous 16-byte pieces (a 1 KB span
+// per wave instruction; read straight into fragments, each instruction
+// would gather 32-byte pieces of 16 rows), then each wave gathers its
+// fragments from LDS. A wave runs alone on its SIMD here, so the address
+// arithmetic before the loads is not hidden: one division per thread, then
+// 32-bit offsets stepped row by row into a buffer over the query tensor.
+//
+// load() issues every load of the thread, with no branch around any of
+// them; the caller may issue other loads before store(), which waits only
+// for these (loads complete in issue order). Rows past the last query row
+// fall past the end of the tensor and read as zero; every slot a lane reads
+// in store() is written first (by the group's rows, the next group's rows or
+// those zeros), and a padding row's partial state is never written. `lds`
+// must be free when store() starts; it is free again on return (after a
+// barrier).
+// Byte offset of query row r of KV head gkv (node r / G, head gkv*G + r % G)
+// in a [node][H_q][D] fp16 tensor, stepped `rs` rows at a time with one
+// division in all (the row step is at most one carry of the head index).
+struct RowWalk {
+    u32 off, step, carry;
+    int h, dh, G;
+    __device__ __forceinline__ RowWalk(const SplitArgs &a, int gkv, int r, int rs, u32 rowb)
+    {
+        const u32 nodeb = (u32)a.H_q * rowb;
+        G = a.G;
+        h = r % G;
+        off = (u32)(r / G) * nodeb + (u32)(gkv * G + h) * rowb;
+        dh = rs % G;
+        step = (u32)(rs / G) * nodeb + (u32)dh * rowb;
+        carry = nodeb - (u32)G * rowb;
+    }
+    __device__ __forceinline__ void next()
+    {
+        h += dh;
+        off += step;
+        const bool wrap = h >= G;
+        h = wrap ? h - G : h;
+        off = wrap ? off + carry : off;
+    }
+};
+
+template <int D, int KVT, int NOWN, int NSH>
+struct QStage {
+    static constexpr int NS = NOWN + NSH;
+    static constexpr int NB = D / 32;
+    static constexpr int QSTR = D + 16;  // row stride (halves): 16 rows x 4 lanes of 2 dwords, 2-way at most
+    static constexpr int NT = 4 * NOWN + NSH;  // tiles of a workgroup
+    static constexpr int PR = D / 8;           // 16-byte pieces per row
+    static constexpr int RS = 256 / PR;        // rows between a thread's pieces
+    static constexpr int NQ = (16 * NT + RS - 1) / RS;  // pieces per thread
+    static_assert(NQ * RS * QSTR <= 2 * Stage<D, KVT>::ELEMS, "staged query rows fit both stages");
+    u4v pc[NQ];
+
+    __device__ __forceinline__ void load(const SplitArgs &a, int gkv, int t0, int tid)
+    {
+        const __amdgpu_buffer_rsrc_t rq = raw_rsrc(a.q, (u32)a.NR * (u32)(2 * D));
+        RowWalk rw(a, gkv, 16 * t0 + tid / PR, RS, 2 * D);
+        const u32 part = 16u * (u32)(tid % PR);
 #pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb) {
-            if constexpr (KVT == TV_KV_Q4_0) {
-                const h4 lo = *(const h4 *)(qr + 32 * bb + 4 * grp);
-                const h4 hi = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
-                h8 f;
-                f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
-                f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
-                qf[bb] = f;
-            } else {
-                qf[bb] = *(const h8 *)(qr + 32 * bb + 8 * grp);
+        for (int j = 0; j < NQ; ++j) {
+            pc[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, rw.off + part, 0, 0);
+            rw.next();
+        }
+    }
+
+    __device__ __forceinline__ void store(int t0, const int (&tile)[NS], int tid, int col, int grp, _Float16 *lds,
+                                          h8 (&qf)[NS][NB]) const
+    {
+        _Float16 *dst = lds + (tid / PR) * QSTR + 8 * (tid % PR);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) *(u4v *)(dst + j * RS * QSTR) = pc[j];
+        __syncthreads();
+        // every LDS read is issued before the first is used (left to itself
+        // the compiler keeps one or two in flight and each waits out the
+        // LDS latency)
+        h4 raw[NS][NB][2];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const _Float16 *qr = lds + (16 * (tile[k] - t0) + col) * QSTR;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                if constexpr (KVT == TV_KV_Q4_0) {
+                    raw[k][bb][0] = *(const h4 *)(qr + 32 * bb + 4 * grp);
+                    raw[k][bb][1] = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
+                } else {
+                    raw[k][bb][0] = *(const h4 *)(qr + 32 * bb + 8 * grp);
+                    raw[k][bb][1] = *(const h4 *)(qr + 32 * bb + 8 * grp + 4);
+                }
             }
         }
-    } else {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb) qf[bb] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k = 0; k < NS; ++k) {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const h4 lo = raw[k][bb][0], hi = raw[k][bb][1];
+                h8 f;
+                if constexpr (KVT == TV_KV_Q4_0) {
+                    f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
+                    f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
+                } else {
+                    f.s0 = lo.x; f.s1 = lo.y; f.s2 = lo.z; f.s3 = lo.w;
+                    f.s4 = hi.x; f.s5 = hi.y; f.s6 = hi.z; f.s7 = hi.w;
+                }
+                qf[k][bb] = f;
+            }
+        }
+        __syncthreads();
     }
-}
+};
 
 // Writes the split's partial state (normalised output, log2 denominator) of
 // every query row. Own tiles go straight to the

@@ -87,8 +87,6 @@ __device__ __forceinline__ void split_half_block(const u32 *r, int b, _Float16 &
     c1 = odd ? r[3] : __builtin_amdgcn_alignbyte(r[3], r[2], 2);
 }
 
-typedef u32 u3v __attribute__((ext_vector_type(3)));
-typedef u32 u4v __attribute__((ext_vector_type(4)));
 
 // Raw-buffer descriptor over one chunk of cache rows: the base moves with the
 // chunk (scalar arithmetic), the per-lane offsets stay constant, and reads
@@ -299,9 +297,25 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 #pragma unroll
     for (int u = 0; u < NSH; ++u) tile[NOWN + u] = tm.t0 + 4 * NOWN + u;
 
+    const int64_t c_begin = split_chunk_begin(a, split);
+    const int64_t c_end = split_chunk_begin(a, split + 1);
+    const u32 magic = 0x64006400u;
+    const int rot = NDQ * w;  // D-tile at loop position j is (j + rot) % NDT
+
+    // prologue: the query rows (from L2) are requested first, the first
+    // chunk's cache bytes (from HBM) next, so that the two are in flight
+    // together and the query rows can be staged before the cache bytes
+    // arrive; then chunk c_begin is dequantised into stage 0 and the raw
+    // bytes of the next are requested
+    QStage<D, TV_KV_Q4_0, NOWN, NSH> qs;
+    qs.load(a, gkv, tm.t0, tid);
+    L ld;
+    ld.init(a, gkv, tid);
+    ld.load_k(a.s0 + c_begin * kChunk);
+    ld.load_v(a.s0 + c_begin * kChunk);
+
     h8 qf[NS][NB];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) load_q_frags<D, TV_KV_Q4_0>(a, gkv, tile[k], tm.t_end, col, grp, qf[k]);
+    qs.store(tm.t0, tile, tid, col, grp, lds, qf);
     // Q fragments are read only as MFMA B operands, which may live in AGPRs;
     // parking them there leaves the VGPRs to the accumulators and the pipeline.
 #pragma unroll
@@ -326,16 +340,6 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 #pragma unroll
         for (int j = 0; j < NDQ; ++j) osh[u][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
-    const int64_t c_begin = a.n_chunks * split / a.S;
-    const int64_t c_end = a.n_chunks * (split + 1) / a.S;
-    const u32 magic = 0x64006400u;
-    const int rot = NDQ * w;  // D-tile at loop position j is (j + rot) % NDT
-
-    L ld;
-    ld.init(a, gkv, tid);
-    // prologue: chunk c_begin dequantised into stage 0, raw bytes of the next
-    ld.load_k(a.s0 + c_begin * kChunk);
-    ld.load_v(a.s0 + c_begin * kChunk);
 #pragma unroll
     for (int j = 0; j < NB; ++j) ld.k_piece(j, lds, magic);
 #pragma unroll
@@ -482,24 +486,51 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 
     // ---- partial states: own tiles by every wave; shared tiles by every
     // wave for its quarter of D (their row maxima and sums are identical in
-    // all waves and written by wave 0)
+    // all waves and written by wave 0). The normalised fp16 rows are gathered
+    // in LDS and written as contiguous 16-byte pieces, a 1 KB span per wave
+    // instruction: stored straight from the fragments, each instruction
+    // would scatter 8-byte pieces over 16 rows, which costs several times
+    // longer per byte. The stores go through buffers over this split's
+    // blocks of the workspace; a row outside this workgroup's rows gets an
+    // out-of-range offset, which drops the store.
+    using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH>;
+    const __amdgpu_buffer_rsrc_t rwo = raw_rsrc(a.ws_o + (int64_t)split * a.NR * D, (u32)a.NR * (u32)(2 * D));
+    const __amdgpu_buffer_rsrc_t rwm = raw_rsrc(a.ws_m + (int64_t)split * a.NR, (u32)a.NR * 4u);
+    __syncthreads();  // every wave is done with the last stage
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
         const float lt = wave_sum_16_32(l[k]);
+        const int rl = 16 * (tile[k] - tm.t0) + col;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        _Float16 *orow = lds + rl * QS::QSTR + 4 * grp;
+        if (k < NOWN) {
+#pragma unroll
+            for (int j = 0; j < NDT; ++j)
+                *(h4 *)(orow + 16 * ((j + rot) & (NDT - 1))) =
+                    __builtin_convertvector(o[k < NOWN ? k : 0][j] * inv, h4);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NDQ; ++j)
+                *(h4 *)(orow + 16 * (j + rot)) = __builtin_convertvector(osh[k >= NOWN ? k - NOWN : 0][j] * inv, h4);
+        }
         const int r = 16 * tile[k] + col;
-        if (tile[k] < tm.t_end && r < a.M) {
-            const int node = r / a.G, h = gkv * a.G + r % a.G;
-            const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-            _Float16 *op = a.ws_o + row * D + 4 * grp;
-            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-            if (k < NOWN) {
+        const bool mwriter = tile[k] < tm.t_end && r < a.M && grp == 0 && (k < NOWN || w == 0);
+        const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(m[k], lt)), rwm,
+                                              mwriter ? rowi * 4u : kOffNone, 0, 0);
+    }
+    __syncthreads();
+    {
+        const int nrows = min(16 * tm.t_end, a.M) - 16 * tm.t0;
+        const int r0 = tid / QS::PR;
+        RowWalk rw(a, gkv, 16 * tm.t0 + r0, QS::RS, 2 * D);
+        const u32 part = 16u * (u32)(tid % QS::PR);
+        const _Float16 *src = lds + r0 * QS::QSTR + 8 * (tid % QS::PR);
 #pragma unroll
-                for (int j = 0; j < NDT; ++j) store_h4(op + 16 * ((j + rot) & (NDT - 1)), o[k < NOWN ? k : 0][j], inv);
-            } else {
-#pragma unroll
-                for (int j = 0; j < NDQ; ++j) store_h4(op + 16 * (j + rot), osh[k >= NOWN ? k - NOWN : 0][j], inv);
-            }
-            if (grp == 0 && (k < NOWN || w == 0)) a.ws_m[row] = partial_lse2(m[k], lt);
+        for (int jj = 0; jj < QS::NQ; ++jj) {
+            const u4v v = *(const u4v *)(src + jj * QS::RS * QS::QSTR);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nrows ? rw.off + part : kOffNone, 0, 0);
+            rw.next();
         }
     }
 }
