@@ -429,7 +429,7 @@ struct MergeArgs {
     // scored here, node i skipping the first head_skip[i] of them
     int64_t head_begin;
     int32_t n_head;
-    uint8_t head_skip[TV_MAX_NODES];
+    int32_t head_skip[TV_MAX_NODES];  // 32-bit entries: a scalar load per node
     // cache rows [tail_begin, tail_end) of the window that do not fill a
     // whole chunk of the split kernel
     const uint8_t *k_cache;
@@ -497,7 +497,10 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int row = blockIdx.x;
-    const int i = row / a.H_q, h = row % a.H_q, g = h / a.G;
+    const int dq = t % QD, sg = t / QD;
+    // the node index is uniform: its ancestor mask and head skip come
+    // through scalar loads, which do not wait behind the vector loads above
+    const int i = __builtin_amdgcn_readfirstlane(row / a.H_q), h = row % a.H_q, g = h / a.G;
     const uint64_t anc = a.anc[i];
     const int na = __builtin_popcountll(anc);
     const int hs = a.head_skip[i];
@@ -510,25 +513,53 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     const uint8_t *kh = a.k_cache + (int64_t)g * a.head_stride;
     const uint8_t *vh = a.v_cache + (int64_t)g * a.head_stride;
 
-    const int dq = t % QD, sg = t / QD;
-    // V values of this group's first extra keys, requested before anything
-    // waits on memory
-    auto extra_v = [&](int kk, float (&vv)[8]) {
-        if (kk < na) {
-            uint64_t mm = anc;
-            for (int r = 0; r < kk; ++r) mm &= mm - 1;
-            const int j = __builtin_ctzll(mm);
-            const h8 vr = *(const h8 *)(a.v_tree + ((int64_t)j * a.H_kv + g) * D + 8 * dq);
-#pragma unroll
-            for (int p = 0; p < 8; ++p) vv[p] = (float)vr[p];
-        } else {
-            cache_values<8>(vh + extra_row(kk) * a.tok_stride, a.kv_type, 8 * dq, vv);
-        }
+    const int kl = t % KL;
+    // row of the kk-th ancestor (kk < na) in the tree's [node][H_kv][D] rows
+    auto tree_row = [&](int kk) -> int64_t {
+        uint64_t mm = anc;
+        for (int r = 0; r < kk; ++r) mm &= mm - 1;
+        return (int64_t)__builtin_ctzll(mm) * a.H_kv + g;
     };
+    // V values of extra key kk, for the cache rows (kk >= na), decoded exactly
+    auto cache_v = [&](int kk, float (&vv)[8]) {
+        cache_values<8>(vh + extra_row(kk) * a.tok_stride, a.kv_type, 8 * dq, vv);
+    };
+    auto cache_k = [&](int kk, float (&kv)[KPT]) {
+        cache_values<KPT>(kh + extra_row(kk) * a.tok_stride, a.kv_type, kl * KPT, kv);
+    };
+    // Requested before anything waits on memory: the V rows of this group's
+    // first extra keys (they do not depend on the scores), the query slice
+    // and the key slices of the first score pass. Tree rows are loaded raw
+    // and converted where they are used, so that no load waits at its branch;
+    // cache rows (window head or tail), decoded where they are loaded, only
+    // occur with a window or a partial last chunk.
     float vpf[VPF][8];
+    h8 vtr[VPF];
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
-        if (sg + NGR * j < nk) extra_v(sg + NGR * j, vpf[j]);
+        const int kk = sg + NGR * j;
+        if (kk < na) vtr[j] = *(const h8 *)(a.v_tree + tree_row(kk) * D + 8 * dq);
+        else if (kk < nk) cache_v(kk, vpf[j]);
+    }
+    typedef _Float16 hk __attribute__((ext_vector_type(KPT)));  // a lane's slice of a row
+    const hk qr = *(const hk *)(a.q + (int64_t)row * D + kl * KPT);
+    const int kk0 = t / KL;
+    hk ktr;
+    float kc0[KPT];
+    if (kk0 < na) ktr = *(const hk *)(a.k_tree + tree_row(kk0) * D + kl * KPT);
+    else if (kk0 < nk) cache_k(kk0, kc0);
+
+    // round 1a's loads for this thread's first SMAX splits, behind those
+    // above (the scores need their loads sooner); no branch around a load: a
+    // split past the last reads split 0, and the fold gives it no weight
+    float mv[SMAX];
+    h8 ov[SMAX];
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k) {
+        const int s = sg + NGR * k;
+        const int64_t base = (int64_t)(s < a.S ? s : 0) * a.NR + row;
+        mv[k] = a.ws_m[base];
+        ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
     }
 
     // ---- round 1a: this thread's splits, folded against their maximum
@@ -536,20 +567,17 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     for (int s0 = sg; s0 < a.S; s0 += NGR * SMAX) {
-        float mv[SMAX];
-        h8 ov[SMAX];
+        if (s0 != sg) {
 #pragma unroll
-        for (int k = 0; k < SMAX; ++k) {
-            const int s = s0 + NGR * k;
-            if (s < a.S) {
-                const int64_t base = (int64_t)s * a.NR + row;
+            for (int k = 0; k < SMAX; ++k) {
+                const int s = s0 + NGR * k;
+                const int64_t base = (int64_t)(s < a.S ? s : 0) * a.NR + row;
                 mv[k] = a.ws_m[base];
                 ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
-            } else {
-                mv[k] = kNegBig;
-                ov[k] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) mv[k] = s0 + NGR * k < a.S ? mv[k] : kNegBig;
         float mb = ms;
 #pragma unroll
         for (int k = 0; k < SMAX; ++k) mb = fmaxf(mb, mv[k]);
@@ -569,24 +597,23 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     // ---- round 1b: scores of the extra keys (ancestors, then tail rows)
     float mk = -INFINITY;
     {
-        const int kl = t % KL;
         float qv[KPT];
 #pragma unroll
-        for (int p = 0; p < KPT; ++p) qv[p] = (float)a.q[(int64_t)row * D + kl * KPT + p];
+        for (int p = 0; p < KPT; ++p) qv[p] = (float)qr[p];
         for (int base = 0; base < nk; base += KPASS) {
             const int kk = base + t / KL;
             float part = 0.f;
             if (kk < nk) {
                 float kv[KPT];
                 if (kk < na) {
-                    uint64_t mm = anc;
-                    for (int r = 0; r < kk; ++r) mm &= mm - 1;
-                    const int j = __builtin_ctzll(mm);
-                    const _Float16 *kr = a.k_tree + ((int64_t)j * a.H_kv + g) * D + kl * KPT;
+                    const hk kr = base == 0 ? ktr : *(const hk *)(a.k_tree + tree_row(kk) * D + kl * KPT);
 #pragma unroll
                     for (int p = 0; p < KPT; ++p) kv[p] = (float)kr[p];
+                } else if (base == 0) {
+#pragma unroll
+                    for (int p = 0; p < KPT; ++p) kv[p] = kc0[p];
                 } else {
-                    cache_values<KPT>(kh + extra_row(kk) * a.tok_stride, a.kv_type, kl * KPT, kv);
+                    cache_k(kk, kv);
                 }
 #pragma unroll
                 for (int p = 0; p < KPT; ++p) part = __builtin_fmaf(qv[p], kv[p], part);
@@ -623,14 +650,20 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
             const float f = exp2f(sk[kk] - mstar);
             L += f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, vpf[j][e], acc[e]);
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, kk < na ? (float)vtr[j][e] : vpf[j][e], acc[e]);
         }
     }
     for (int kk = sg + NGR * VPF; kk < nk; kk += NGR) {
         const float f = exp2f(sk[kk] - mstar);
         L += f;
         float vv[8];
-        extra_v(kk, vv);
+        if (kk < na) {
+            const h8 vr = *(const h8 *)(a.v_tree + tree_row(kk) * D + 8 * dq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = (float)vr[e];
+        } else {
+            cache_v(kk, vv);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f, vv[e], acc[e]);
     }
@@ -751,7 +784,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
             const int64_t start = d->n_ctx + depth - d->window;
             int64_t skip = start - plan.s0;
             skip = skip < 0 ? 0 : (skip > plan.head ? plan.head : skip);
-            mg.head_skip[i] = (uint8_t)skip;
+            mg.head_skip[i] = (int32_t)skip;
             const int64_t first = (int64_t)depth - d->window;  // shallowest ancestor depth kept
             if (first > 0) {
                 int du = depth;
