@@ -119,22 +119,24 @@ __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
     const int lane = threadIdx.x;
     const int n = a.n;
     const bool live = lane < n;
+    // the slice maxima of row `lane` (a dead lane reads row 0), loaded 32 at a
+    // time with no branch around a load, so that the first 32 are in flight
+    // together with the per-lane argument reads below
+    const uint64_t *pr = a.part + (int64_t)(live ? lane : 0) * a.n_slices;
+    uint64_t b = 0;
+    for (int s0 = 0; s0 < a.n_slices; s0 += 32) {
+        uint64_t v[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) v[k] = pr[s0 + k < a.n_slices ? s0 + k : 0];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) b = umax64(b, v[k]);
+    }
     const int par = live ? a.parent[lane] : -1;
     const int tok = live ? a.tokens[lane] : -1;
     const uint64_t anc = live ? a.anc[lane] : 0ull;
 
     int am = 0;
     if (live) {
-        // the slice maxima of row `lane`, loaded 32 at a time
-        uint64_t b = 0;
-        const uint64_t *pr = a.part + (int64_t)lane * a.n_slices;
-        for (int s0 = 0; s0 < a.n_slices; s0 += 32) {
-            uint64_t v[32];
-#pragma unroll
-            for (int k = 0; k < 32; ++k) v[k] = s0 + k < a.n_slices ? pr[s0 + k] : 0ull;
-#pragma unroll
-            for (int k = 0; k < 32; ++k) b = umax64(b, v[k]);
-        }
         am = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFu));
         a.argmax_out[lane] = am;
     }

@@ -405,7 +405,7 @@ split_kernel(const SplitArgs a)
     }
 
     static_assert(NSH * 4 * 16 * (D + 2) * 4 <= 2 * St::ELEMS * 2, "merge scratch");
-    write_partials<D, NOWN, NSH>(a, lds, 2 * St::ELEMS * 2, tid, w, col, grp, gkv, split, t_end, tile, o, m, l);
+    write_partials<D, NOWN, NSH>(a, lds, 2 * St::ELEMS * 2, tid, w, col, grp, gkv, split, tm.t0, t_end, tile, o, m, l);
 }
 
 // ---------------------------------------------------------------------------

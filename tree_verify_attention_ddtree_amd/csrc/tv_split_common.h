@@ -310,35 +310,32 @@ struct QStage {
 };
 
 // Writes the split's partial state (normalised output, log2 denominator) of
-// every query row. Own tiles go straight to the
-// workspace; the four waves' partial states of a shared tile are combined
-// through LDS (`scratch`, at least scratch_bytes long, free once called).
+// every query row, for the F16 split kernel. `scratch` is the kernel's LDS
+// (both stages, at least scratch_bytes long), free once every wave is past
+// the last chunk. Shared tiles first: the four waves' partial states of a
+// shared tile (each wave scored a quarter of the keys) are combined through
+// LDS and written element by element (consecutive threads, consecutive
+// values). Then the own tiles: their normalised fp16 rows are gathered in LDS
+// and written as contiguous 16-byte pieces, a 1 KB span per wave instruction
+// (stored straight from the fragments, each instruction would scatter 8-byte
+// pieces over 16 rows). Stores go through buffers over this split's blocks of
+// the workspace; a row that is not this workgroup's own gets an out-of-range
+// offset, which drops the store.
 template <int D, int NOWN, int NSH>
 __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scratch, int scratch_bytes, int tid,
-                                               int w, int col, int grp, int gkv, int split, int t_end,
+                                               int w, int col, int grp, int gkv, int split, int t0, int t_end,
                                                const int (&tile)[NOWN + NSH], f4 (&o)[NOWN + NSH][D / 16],
                                                float (&m)[NOWN + NSH], float (&l)[NOWN + NSH])
 {
     constexpr int NDT = D / 16;
-#pragma unroll
-    for (int k = 0; k < NOWN; ++k) {
-        const float lt = wave_sum_16_32(l[k]);
-        const int r = 16 * tile[k] + col;
-        if (tile[k] < t_end && r < a.M) {
-            const int node = r / a.G, h = gkv * a.G + r % a.G;
-            const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-            _Float16 *op = a.ws_o + row * D + 4 * grp;
-            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) store_h4(op + 16 * dt, o[k][dt], inv);
-            if (grp == 0) a.ws_m[row] = partial_lse2(m[k], lt);
-        }
-    }
+    using QS = QStage<D, TV_KV_F16, NOWN, NSH>;
+    (void)scratch_bytes;
+    const __amdgpu_buffer_rsrc_t rwo = raw_rsrc(a.ws_o + (int64_t)split * a.NR * D, (u32)a.NR * (u32)(2 * D));
+    const __amdgpu_buffer_rsrc_t rwm = raw_rsrc(a.ws_m + (int64_t)split * a.NR, (u32)a.NR * 4u);
+    __syncthreads();  // every wave is done with the K/V stages
     if constexpr (NSH > 0) {
-        __syncthreads();  // every wave is done with the K/V stages
         float *so = (float *)scratch;            // [NSH][4][16][D]
         float *sml = so + NSH * 4 * 16 * D;      // [NSH][4][16][2]
-        (void)scratch_bytes;
 #pragma unroll
         for (int u = 0; u < NSH; ++u) {
             const float lt = wave_sum_16_32(l[NOWN + u]);
@@ -356,7 +353,6 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
             for (int e = tid; e < 16 * D; e += 256) {
                 const int qr = e / D, d = e % D;
                 const int r = 16 * tile[NOWN + u] + qr;
-                if (r >= a.M) continue;
                 float mw[4], mx = kNegBig;
 #pragma unroll
                 for (int ww = 0; ww < 4; ++ww) {
@@ -370,11 +366,44 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
                     acc += f * so[((u * 4 + ww) * 16 + qr) * D + d];
                     lsum += f * sml[((u * 4 + ww) * 16 + qr) * 2 + 1];
                 }
-                const int node = r / a.G, h = gkv * a.G + r % a.G;
-                const int64_t row = (int64_t)split * a.NR + (int64_t)node * a.H_q + h;
-                a.ws_o[row * D + d] = (_Float16)(lsum > 0.f ? acc / lsum : 0.f);
-                if (d == 0) a.ws_m[row] = partial_lse2(mx, lsum);
+                const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
+                const bool valid = r < a.M;
+                const _Float16 v = (_Float16)(lsum > 0.f ? acc / lsum : 0.f);
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rwo,
+                                                      valid ? rowi * (u32)(2 * D) + 2u * (u32)d : kOffNone, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(mx, lsum)), rwm,
+                                                      valid && d == 0 ? rowi * 4u : kOffNone, 0, 0);
             }
+        }
+        __syncthreads();  // the scratch is free again
+    }
+    // own tiles: normalised fp16 rows into LDS, then contiguous stores
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) {
+        const float lt = wave_sum_16_32(l[k]);
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        _Float16 *orow = scratch + (16 * (tile[k] - t0) + col) * QS::QSTR + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *(h4 *)(orow + 16 * dt) = __builtin_convertvector(o[k][dt] * inv, h4);
+        const int r = 16 * tile[k] + col;
+        const bool mwriter = tile[k] < t_end && r < a.M && grp == 0;
+        const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(m[k], lt)), rwm,
+                                              mwriter ? rowi * 4u : kOffNone, 0, 0);
+    }
+    __syncthreads();
+    {
+        // own rows are the first 16 * 4 * NOWN of the group (tiles t0 + 4k + w)
+        const int nown_rows = min(min(16 * t_end, a.M) - 16 * t0, 16 * 4 * NOWN);
+        const int r0 = tid / QS::PR;
+        RowWalk rw(a, gkv, 16 * t0 + r0, QS::RS, 2 * D);
+        const u32 part = 16u * (u32)(tid % QS::PR);
+        const _Float16 *src = scratch + r0 * QS::QSTR + 8 * (tid % QS::PR);
+#pragma unroll
+        for (int jj = 0; jj < QS::NQ; ++jj) {
+            const u4v v = *(const u4v *)(src + jj * QS::RS * QS::QSTR);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nown_rows ? rw.off + part : kOffNone, 0, 0);
+            rw.next();
         }
     }
 }
