@@ -58,26 +58,31 @@ static int check_desc(const tv_attn_desc *d)
     return TV_OK;
 }
 
+// Tile roles for T tiles cut into RG row groups; false when a group needs
+// more tile slots per wave than the kernels have.
+static bool rows_for_groups(int T, int RG, RowPlan *rp)
+{
+    int nown = 0, nsh = 0;
+    for (int g = 0; g < RG; ++g) {
+        const int Tg = T / RG + (g < T % RG ? 1 : 0);
+        int o, s;
+        group_roles(Tg, &o, &s);
+        nown = o > nown ? o : nown;
+        nsh = s > nsh ? s : nsh;
+    }
+    if (nown + nsh > kMaxSlots || nown + nsh < 1) return false;
+    rp->tiles = T;
+    rp->groups = RG;
+    rp->nown = nown;
+    rp->nsh = nsh;
+    return true;
+}
+
 static int plan_rows(int M, RowPlan *rp)
 {
     const int T = (M + 15) / 16;
-    for (int RG = 1; RG <= T; ++RG) {
-        int nown = 0, nsh = 0;
-        for (int g = 0; g < RG; ++g) {
-            const int Tg = T / RG + (g < T % RG ? 1 : 0);
-            int o, s;
-            group_roles(Tg, &o, &s);
-            nown = o > nown ? o : nown;
-            nsh = s > nsh ? s : nsh;
-        }
-        if (nown + nsh <= kMaxSlots && nown + nsh >= 1) {
-            rp->tiles = T;
-            rp->groups = RG;
-            rp->nown = nown;
-            rp->nsh = nsh;
-            return TV_OK;
-        }
-    }
+    for (int RG = 1; RG <= T; ++RG)
+        if (rows_for_groups(T, RG, rp)) return TV_OK;
     return TV_E_SHAPE;
 }
 
@@ -118,6 +123,15 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     if (S < 1) S = 1;
     if (S > 65535) S = 65535;
     out->S = (int)S;
+    // A key range too short to give every CU a split (S capped by the chunk
+    // count, e.g. a 2048-row window) leaves CUs idle: cut the rows into more
+    // groups as well, up to one workgroup per CU. Each group dequantises the
+    // same chunks again, but on a CU that would otherwise wait.
+    for (int RG = out->rows.groups + 1; RG <= out->rows.tiles; ++RG) {
+        if ((int64_t)out->S * d->n_kv_heads * RG > n_cu) break;
+        RowPlan rp;
+        if (rows_for_groups(out->rows.tiles, RG, &rp)) out->rows = rp;
+    }
     return TV_OK;
 }
 
