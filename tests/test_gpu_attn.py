@@ -235,3 +235,19 @@ def test_per_position_window_61k_and_deep_chain():
                                 seed=77, kv="q4_0", parent=synth.chain_tree(64)), window=10, window_mode=1)
     err = rownorm_err(gpu_attn(ch).astype(np.float64), oracle.attn(ch))
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_remainder_rows_left_to_merge_kernel(kv, mode):
+    """With 16 KV heads the grid has 16 splits per head (256 CUs); 16415 cache
+    rows are 256 whole chunks, 16 to a split, plus 31 rows. A remainder chunk
+    would make one split longer, so the merge kernel scores those 31 rows.
+    With a per-position window over the whole cache the split kernel also
+    masks, per node, the first rows of its first chunk."""
+    inp = synth.attn_inputs(n_q_heads=16, n_kv_heads=16, head_dim=64, n_ctx=16415, n_nodes=12, depth_cap=8,
+                            seed=4242 + mode, kv=kv)
+    if mode:
+        inp = dict(inp, window=16415, window_mode=1)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err

@@ -94,35 +94,64 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     if (rc) return rc;
     out->s0 = (d->window > 0 && d->n_ctx > d->window) ? d->n_ctx - d->window : 0;
     out->R = d->n_ctx - out->s0;
-    // per-position window: the first rows of the window, where the nodes'
-    // windows start at different rows (a node at depth k starts k rows after
-    // a root, so they span the tree's depth), go to the merge kernel, which
-    // scores them per node
-    out->head = 0;
-    if (d->window_mode == 1 && d->window > 0) {
-        int depth[TV_MAX_NODES], max_depth = 0;
+    int max_depth = 0;
+    const bool per_pos = d->window_mode == 1 && d->window > 0;
+    if (per_pos) {
+        int depth[TV_MAX_NODES];
         depth[0] = 0;
         for (int i = 1; i < d->n_nodes; ++i) {
             depth[i] = depth[d->parent[i]] + 1;
             max_depth = depth[i] > max_depth ? depth[i] : max_depth;
         }
-        out->head = out->R < max_depth ? out->R : max_depth;
-    }
-    // whole chunks of the rest go to the split kernel; its last
-    // (R - head) % kChunk rows are attended by the merge kernel with the tree
-    out->n_chunks = (out->R - out->head) / kChunk;
-    if (out->n_chunks == 0) {
-        out->S = 0;
-        return TV_OK;
     }
     const int64_t per = (int64_t)d->n_kv_heads * out->rows.groups;
-    int64_t S = (n_cu + per - 1) / per;
-    int64_t cap = out->n_chunks / kMinChunks;
-    if (cap < 1) cap = 1;
-    if (S > cap) S = cap;
-    if (S < 1) S = 1;
-    if (S > 65535) S = 65535;
-    out->S = (int)S;
+    auto splits = [&](int64_t n_chunks) -> int {
+        int64_t S = (n_cu + per - 1) / per;
+        int64_t cap = n_chunks / kMinChunks;
+        if (cap < 1) cap = 1;
+        if (S > cap) S = cap;
+        if (S < 1) S = 1;
+        if (S > 65535) S = 65535;
+        return (int)S;
+    };
+    // Two ways to attend the window rows that do not make a whole chunk of
+    // the same keys for every row: the per-node first rows of a per-position
+    // window (as many as the tree is deep) and a remainder of fewer than
+    // kChunk rows at the window's end.
+    //  - masked split kernel: whole chunks from s0, then one chunk ending at
+    //    the window's end; per row, keys it may not see (before its node's
+    //    window start, or already counted) score -inf. The masking code
+    //    costs every chunk about 3% (register allocation), so it is a
+    //    separate instantiation, taken while splits are short (up to 8
+    //    chunks), where the merge kernel's rows would cost more.
+    //  - otherwise the merge kernel scores those rows (head rows per node,
+    //    then the tail) and the split kernel takes the whole chunks between.
+    out->mask = 0;
+    out->tail = 0;
+    const int64_t rem = out->R % kChunk;
+    const bool ragged = rem > 0 || (per_pos && max_depth > 0 && out->R > 0);
+    if (ragged && d->n_ctx >= kChunk) {
+        const int64_t nc = out->R / kChunk + (rem ? 1 : 0);
+        const int S = splits(nc);
+        if ((nc + S - 1) / S <= 8) {
+            out->mask = 1;
+            out->head = 0;
+            out->n_whole = out->R / kChunk;
+            out->n_chunks = nc;
+            out->S = S;
+        }
+    }
+    if (!out->mask) {
+        out->head = per_pos ? (out->R < max_depth ? out->R : max_depth) : 0;
+        out->n_chunks = (out->R - out->head) / kChunk;
+        out->n_whole = out->n_chunks;
+        out->tail = out->R - out->head - out->n_chunks * kChunk;
+        if (out->n_chunks == 0) {
+            out->S = 0;
+            return TV_OK;
+        }
+        out->S = splits(out->n_chunks);
+    }
     // A key range too short to give every CU a split (S capped by the chunk
     // count, e.g. a 2048-row window) leaves CUs idle: cut the rows into more
     // groups as well, up to one workgroup per CU. Each group dequantises the

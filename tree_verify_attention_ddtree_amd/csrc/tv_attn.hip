@@ -192,7 +192,7 @@ __device__ __forceinline__ void store_stage(const u32 *raw, _Float16 *ks, _Float
     }
 }
 
-template <int D, int KVT, int NOWN, int NSH>
+template <int D, int KVT, int NOWN, int NSH, bool MASK>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 split_kernel(const SplitArgs a)
 {
@@ -228,7 +228,7 @@ split_kernel(const SplitArgs a)
     qs.load(a, gkv, tm.t0, tid);
     // (every split has at least one chunk: the plan keeps S <= n_chunks)
     u32 raw[St::RAW];
-    load_raw<D, KVT>(a, gkv, a.s0 + c_begin * kChunk, tid, raw);
+    load_raw<D, KVT>(a, gkv, chunk_row<MASK>(a, c_begin), tid, raw);
 
     h8 qf[NS][NB];
     qs.store(tm.t0, tile, tid, col, grp, lds, qf);
@@ -254,7 +254,7 @@ split_kernel(const SplitArgs a)
         _Float16 *ks = lds + st * St::ELEMS;
         _Float16 *vt = ks + St::KELEMS;
         store_stage<D, KVT>(raw, ks, vt, tid);
-        if (c + 1 < c_end) load_raw<D, KVT>(a, gkv, a.s0 + (c + 1) * kChunk, tid, raw);
+        if (c + 1 < c_end) load_raw<D, KVT>(a, gkv, chunk_row<MASK>(a, c + 1), tid, raw);
         __syncthreads();
 
 
@@ -291,6 +291,19 @@ split_kernel(const SplitArgs a)
             for (int u = 0; u < NSH; ++u)
                 ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[bb & 1][4], qf[NOWN + u][bb], ssh[u], 0, 0, 0);
             TV_SCHED_FENCE();
+        }
+        if constexpr (MASK) {
+            if (chunk_masked(a, c)) {
+#pragma unroll
+                for (int k = 0; k < NOWN; ++k) {
+                    const int thr = masked_keys(a, c, row_skip(a, tile[k], t_end, col));
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) mask_tile(sacc[k][kt], kt, grp, thr);
+                }
+#pragma unroll
+                for (int u = 0; u < NSH; ++u)
+                    mask_tile(ssh[u], w, grp, masked_keys(a, c, row_skip(a, tile[NOWN + u], t_end, col)));
+            }
         }
 
         // ---- online softmax -> fp16 P^T fragments
@@ -686,26 +699,29 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 // Host side.
 
 
-template <int D, int KVT>
+template <int D, int KVT, bool MASK>
 static split_fn pick_split(int nown, int nsh)
 {
 #define TV_CASE(O, S)              \
-    if (nown == O && nsh == S) return split_kernel<D, KVT, O, S>;
+    if (nown == O && nsh == S) return split_kernel<D, KVT, O, S, MASK>;
     TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
     TV_CASE(3, 0)
 #undef TV_CASE
     return nullptr;
 }
 
-static split_fn pick_split(int D, int kv, int nown, int nsh)
+template <int D>
+static split_fn pick_split_f16(int nown, int nsh, bool mask)
 {
-    if (kv == TV_KV_Q4_0) {
-        return pick_split_q4(D, nown, nsh);
-    } else {
-        if (D == 64) return pick_split<64, TV_KV_F16>(nown, nsh);
-        if (D == 128) return pick_split<128, TV_KV_F16>(nown, nsh);
-        if (D == 256) return pick_split<256, TV_KV_F16>(nown, nsh);
-    }
+    return mask ? pick_split<D, TV_KV_F16, true>(nown, nsh) : pick_split<D, TV_KV_F16, false>(nown, nsh);
+}
+
+static split_fn pick_split(int D, int kv, int nown, int nsh, bool mask)
+{
+    if (kv == TV_KV_Q4_0) return pick_split_q4(D, nown, nsh, mask);
+    if (D == 64) return pick_split_f16<64>(nown, nsh, mask);
+    if (D == 128) return pick_split_f16<128>(nown, nsh, mask);
+    if (D == 256) return pick_split_f16<256>(nown, nsh, mask);
     return nullptr;
 }
 
@@ -729,7 +745,8 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         a.ws_o = ws_o;
         a.ws_m = ws_m;
         a.s0 = plan.s0 + plan.head;
-        a.key_end = plan.s0 + plan.R;
+        a.n_whole = plan.n_whole;
+        a.last_start = plan.s0 + plan.R - kChunk;
         a.c_per = plan.n_chunks / plan.S;
         a.c_rem = (int32_t)(plan.n_chunks % plan.S);
         a.NR = NR;
@@ -738,7 +755,21 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         a.M = G * n;
         a.S = plan.S;
         a.c = c;
-        split_fn fn = pick_split(D, d->kv_type, plan.rows.nown, plan.rows.nsh);
+        a.has_skip = 0;
+        for (int i = 0; i < TV_MAX_NODES; ++i) a.skip[i] = 0;
+        if (plan.mask && d->window_mode == 1 && d->window > 0) {
+            // per-position window: the node at depth k sees positions from
+            // n_ctx + k - W on
+            for (int i = 0; i < n; ++i) {
+                int depth = 0;
+                for (int u = d->parent[i]; u >= 0; u = d->parent[u]) ++depth;
+                int64_t skip = d->n_ctx + depth - d->window - plan.s0;
+                skip = skip < 0 ? 0 : (skip > plan.R ? plan.R : skip);
+                a.skip[i] = (int32_t)skip;
+                a.has_skip |= skip > 0;
+            }
+        }
+        split_fn fn = pick_split(D, d->kv_type, plan.rows.nown, plan.rows.nsh, plan.mask != 0);
         if (!fn) return TV_E_SHAPE;
         dim3 grid(plan.S, Hkv, plan.rows.groups);
         void *args[] = {(void *)&a};
@@ -762,10 +793,12 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
     mg.v_cache = (const uint8_t *)p->v_cache;
     mg.tok_stride = d->kv_token_stride;
     mg.head_stride = d->kv_head_stride;
+    // window rows left to the merge kernel: per-node head rows, then the
+    // tail (none when the masked split kernel took every row)
     mg.head_begin = plan.s0;
     mg.n_head = (int32_t)plan.head;
-    mg.tail_begin = plan.s0 + plan.head + plan.n_chunks * kChunk;
-    mg.n_tail = (int32_t)(plan.R - plan.head - plan.n_chunks * kChunk);
+    mg.tail_begin = plan.s0 + plan.R - plan.tail;
+    mg.n_tail = (int32_t)plan.tail;
     mg.kv_type = d->kv_type;
     for (int i = 0; i < TV_MAX_NODES; ++i) {
         mg.anc[i] = 0;
@@ -778,7 +811,7 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
             mk |= 1ull << u;
             ++depth;
         }
-        if (plan.head > 0) {
+        if (d->window_mode == 1 && d->window > 0) {
             // per-position window: the node at depth k sees positions from
             // n_ctx + k - W on, in the cache and along its path
             const int64_t start = d->n_ctx + depth - d->window;

@@ -42,7 +42,10 @@ struct SplitPlan {
     int64_t s0;       // first cache row in the window
     int64_t R;        // cache rows in the window
     int64_t head;     // rows [s0, s0 + head) scored per node by the merge kernel (<= tree depth)
-    int64_t n_chunks; // whole chunks of the rest: (R - head) / kChunk
+    int64_t n_chunks; // chunks of the split kernel (from s0 + head)
+    int64_t n_whole;  // of which whole chunks; a chunk after them ends at the window's end
+    int64_t tail;     // last rows of the window scored by the merge kernel
+    int mask;         // the split kernel masks keys (its last chunk, per-node window starts)
     int S;            // key-range splits per (KV head, row group)
 };
 

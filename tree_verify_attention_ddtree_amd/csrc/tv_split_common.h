@@ -46,8 +46,9 @@ struct SplitArgs {
     const _Float16 *q;
     _Float16 *ws_o;  // [S][NR][D] partial outputs, each divided by its row sum
     float *ws_m;     // [S][NR] log2 of the partial's softmax denominator
-    int64_t s0;
-    int64_t key_end;  // end of the rows covered by whole chunks
+    int64_t s0;          // first row of the split kernel's chunks
+    int64_t n_whole;     // whole chunks from s0; a chunk after them (masked kernels) ends at the window's end
+    int64_t last_start;  // first row of that chunk
     int64_t c_per;  // whole chunks per split: n_chunks / S
     int32_t c_rem;  // n_chunks % S
     int32_t NR;     // n * H_q
@@ -56,7 +57,55 @@ struct SplitArgs {
     int32_t M;  // G * n
     int32_t S;
     float c;  // scale * log2(e)
+    // masked kernels, per-position window: node i sees the window from row
+    // s0 + skip[i] on
+    int32_t has_skip;
+    int32_t skip[TV_MAX_NODES];
 };
+
+// First cache row of chunk c: whole chunks from s0; for the masked kernels,
+// then the chunk that ends at the window's end.
+template <bool MASK>
+__device__ __forceinline__ int64_t chunk_row(const SplitArgs &a, int64_t c)
+{
+    if constexpr (MASK) return c < a.n_whole ? a.s0 + c * kChunk : a.last_start;
+    return a.s0 + c * kChunk;
+}
+
+// Whether chunk c holds keys some query row may not see: the first chunk of
+// a per-position window, and the chunk that ends at the window's end (its
+// rows before the end of the whole chunks are already counted).
+__device__ __forceinline__ bool chunk_masked(const SplitArgs &a, int64_t c)
+{
+    return c == a.n_whole || (c == 0 && a.has_skip);
+}
+
+// Offset from s0 of the first window row that a slot's query row sees (0 for
+// padding rows), computed where a masked chunk needs it.
+__device__ __forceinline__ int row_skip(const SplitArgs &a, int tile, int t_end, int col)
+{
+    const int r = 16 * tile + col;
+    return (a.has_skip && tile < t_end && r < a.M) ? a.skip[r / a.G] : 0;
+}
+
+// In a masked chunk, the count of leading keys a row may not see: those
+// before its first visible row or before the end of the whole chunks.
+__device__ __forceinline__ int masked_keys(const SplitArgs &a, int64_t c, int skip)
+{
+    const int64_t cs = chunk_row<true>(a, c);
+    const int64_t floor_row = c == a.n_whole ? a.s0 + a.n_whole * kChunk : a.s0;
+    const int64_t first = a.s0 + skip > floor_row ? a.s0 + skip : floor_row;
+    return (int)(first - cs);
+}
+
+// Scores of key tile kt of a 16x16 S^T tile (lane (col, grp) holds keys
+// 16kt + 4grp + e of row col) below `thr` become -inf; exp2 makes them 0.
+__device__ __forceinline__ void mask_tile(f4 &s, int kt, int grp, int thr)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (16 * kt + 4 * grp + e < thr) s[e] = -INFINITY;
+}
 
 // First chunk of split s (s = S gives n_chunks): floor(n_chunks * s / S),
 // written as s * c_per + floor(s * c_rem / S) so that it needs no 64-bit
@@ -408,6 +457,6 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
     }
 }
 
-split_fn pick_split_q4(int D, int nown, int nsh);
+split_fn pick_split_q4(int D, int nown, int nsh, bool mask);
 
 }  // namespace tv

@@ -129,9 +129,9 @@ struct Q4Loader {
         voff_w = vrow + (u32)window_off(vb, vh);
     }
 
-    // Every key of a chunk is a committed row (the tail of the window that
-    // does not fill a chunk is left to the merge kernel), so no bounds checks
-    // beyond the descriptor's.
+    // Every row of a chunk is a cache row (a window's remainder is either
+    // read as the chunk that ends at the window's end or left to the merge
+    // kernel), so no bounds checks beyond the descriptor's.
     __device__ __forceinline__ void load_k(int64_t chunk_row)
     {
         const __amdgpu_buffer_rsrc_t r = chunk_rsrc(kbase + chunk_row * tok_stride, chunk_bytes);
@@ -271,7 +271,7 @@ struct Q4Loader {
 // wave walks the D-tiles rotated by its index, so that its shared quarter is
 // the first NDT/4 positions of every k-step and every index into the
 // register arrays stays a compile-time constant.
-template <int D, int NOWN, int NSH>
+template <int D, int NOWN, int NSH, bool MASK>
 __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 {
     using St = Stage<D, TV_KV_Q4_0>;
@@ -311,8 +311,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     qs.load(a, gkv, tm.t0, tid);
     L ld;
     ld.init(a, gkv, tid);
-    ld.load_k(a.s0 + c_begin * kChunk);
-    ld.load_v(a.s0 + c_begin * kChunk);
+    ld.load_k(chunk_row<MASK>(a, c_begin));
+    ld.load_v(chunk_row<MASK>(a, c_begin));
 
     h8 qf[NS][NB];
     qs.store(tm.t0, tile, tid, col, grp, lds, qf);
@@ -345,8 +345,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 #pragma unroll
     for (int p = 0; p < L::V_PIECES; ++p) ld.v_piece(p, lds + St::KELEMS, magic);
     if (c_begin + 1 < c_end) {
-        ld.load_k(a.s0 + (c_begin + 1) * kChunk);
-        ld.load_v(a.s0 + (c_begin + 1) * kChunk);
+        ld.load_k(chunk_row<MASK>(a, c_begin + 1));
+        ld.load_v(chunk_row<MASK>(a, c_begin + 1));
     }
 
     for (int64_t c = c_begin; c < c_end; ++c) {
@@ -387,7 +387,17 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                 TV_SCHED_FENCE();
             }
         }
-        if (c + 2 < c_end) ld.load_k(a.s0 + (c + 2) * kChunk);
+        if (c + 2 < c_end) ld.load_k(chunk_row<MASK>(a, c + 2));
+        if constexpr (MASK) {
+            if (chunk_masked(a, c)) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) {
+                    const int thr = masked_keys(a, c, row_skip(a, tile[k], tm.t_end, col));
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) mask_tile(sacc[k][kt], kt, grp, thr);
+                }
+            }
+        }
 
         // ---- running maxima (trees: the VALU's dependent-issue latency is
         // long), one wave-uniform branch for the rare rescale of all slots
@@ -481,7 +491,7 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                 TV_SCHED_FENCE();
             }
         }
-        if (c + 2 < c_end) ld.load_v(a.s0 + (c + 2) * kChunk);
+        if (c + 2 < c_end) ld.load_v(chunk_row<MASK>(a, c + 2));
     }
 
     // ---- partial states: own tiles by every wave; shared tiles by every
@@ -535,22 +545,22 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     }
 }
 
-template <int D>
+template <int D, bool MASK>
 static split_fn pick_q4(int nown, int nsh)
 {
 #define TV_CASE(O, S) \
-    if (nown == O && nsh == S) return split_q4_kernel<D, O, S>;
+    if (nown == O && nsh == S) return split_q4_kernel<D, O, S, MASK>;
     TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
     TV_CASE(3, 0)
 #undef TV_CASE
     return nullptr;
 }
 
-split_fn pick_split_q4(int D, int nown, int nsh)
+split_fn pick_split_q4(int D, int nown, int nsh, bool mask)
 {
-    if (D == 64) return pick_q4<64>(nown, nsh);
-    if (D == 128) return pick_q4<128>(nown, nsh);
-    if (D == 256) return pick_q4<256>(nown, nsh);
+    if (D == 64) return mask ? pick_q4<64, true>(nown, nsh) : pick_q4<64, false>(nown, nsh);
+    if (D == 128) return mask ? pick_q4<128, true>(nown, nsh) : pick_q4<128, false>(nown, nsh);
+    if (D == 256) return mask ? pick_q4<256, true>(nown, nsh) : pick_q4<256, false>(nown, nsh);
     return nullptr;
 }
 
