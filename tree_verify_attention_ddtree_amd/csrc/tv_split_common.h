@@ -315,44 +315,39 @@ struct QStage {
     __device__ __forceinline__ void store(int t0, const int (&tile)[NS], int tid, int col, int grp, _Float16 *lds,
                                           h8 (&qf)[NS][NB]) const
     {
-        _Float16 *dst = lds + (tid / PR) * QSTR + 8 * (tid % PR);
+        if constexpr (KVT == TV_KV_Q4_0) {
+            // Rows go to LDS already in the fragments' element order, so that
+            // a fragment is one 16-byte read: in block bb, lane group g reads
+            // elements 4g + (0, 2, 1, 3), then 16 + 4g + (0, 2, 1, 3) (the
+            // order of q4_unpack). This thread's piece holds elements 8s .. 8s+7
+            // of block bb; its half h (4 elements, two dwords) is reordered by
+            // two byte permutes and lands at 8 ((2s + h) mod 4) + 4 (s / 2).
+            const int q = tid % PR, bb = q / 4, sub = q % 4;
+            _Float16 *dst = lds + (tid / PR) * QSTR + 32 * bb;
+            const int pos0 = 8 * ((2 * sub) % 4) + 4 * (sub / 2);
+            const int pos1 = 8 * ((2 * sub + 1) % 4) + 4 * (sub / 2);
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) *(u4v *)(dst + j * RS * QSTR) = pc[j];
+            for (int j = 0; j < NQ; ++j) {
+                const u4v v = pc[j];
+                const u2v h0 = {__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[1], v[0], 0x07060302u)};
+                const u2v h1 = {__builtin_amdgcn_perm(v[3], v[2], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+                *(u2v *)(dst + j * RS * QSTR + pos0) = h0;
+                *(u2v *)(dst + j * RS * QSTR + pos1) = h1;
+            }
+        } else {
+            _Float16 *dst = lds + (tid / PR) * QSTR + 8 * (tid % PR);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) *(u4v *)(dst + j * RS * QSTR) = pc[j];
+        }
         __syncthreads();
         // every LDS read is issued before the first is used (left to itself
         // the compiler keeps one or two in flight and each waits out the
         // LDS latency)
-        h4 raw[NS][NB][2];
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            const _Float16 *qr = lds + (16 * (tile[k] - t0) + col) * QSTR;
+            const _Float16 *qr = lds + (16 * (tile[k] - t0) + col) * QSTR + 8 * grp;
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                if constexpr (KVT == TV_KV_Q4_0) {
-                    raw[k][bb][0] = *(const h4 *)(qr + 32 * bb + 4 * grp);
-                    raw[k][bb][1] = *(const h4 *)(qr + 32 * bb + 16 + 4 * grp);
-                } else {
-                    raw[k][bb][0] = *(const h4 *)(qr + 32 * bb + 8 * grp);
-                    raw[k][bb][1] = *(const h4 *)(qr + 32 * bb + 8 * grp + 4);
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                const h4 lo = raw[k][bb][0], hi = raw[k][bb][1];
-                h8 f;
-                if constexpr (KVT == TV_KV_Q4_0) {
-                    f.s0 = lo.x; f.s1 = lo.z; f.s2 = lo.y; f.s3 = lo.w;
-                    f.s4 = hi.x; f.s5 = hi.z; f.s6 = hi.y; f.s7 = hi.w;
-                } else {
-                    f.s0 = lo.x; f.s1 = lo.y; f.s2 = lo.z; f.s3 = lo.w;
-                    f.s4 = hi.x; f.s5 = hi.y; f.s6 = hi.z; f.s7 = hi.w;
-                }
-                qf[k][bb] = f;
-            }
+            for (int bb = 0; bb < NB; ++bb) qf[k][bb] = *(const h8 *)(qr + 32 * bb);
         }
         __syncthreads();
     }
