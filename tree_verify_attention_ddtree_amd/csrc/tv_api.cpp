@@ -129,7 +129,10 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     out->mask = 0;
     out->tail = 0;
     const int64_t rem = out->R % kChunk;
-    const bool ragged = rem > 0 || (per_pos && max_depth > 0 && out->R > 0);
+    // a node at depth k starts seeing the window k - (W - R) rows in: some
+    // node skips rows when the tree is deeper than W - R
+    const bool skips = per_pos && out->R > 0 && max_depth > d->window - out->R;
+    const bool ragged = rem > 0 || skips;
     if (ragged && d->n_ctx >= kChunk) {
         const int64_t nc = out->R / kChunk + (rem ? 1 : 0);
         const int S = splits(nc);

@@ -241,27 +241,6 @@ struct TileMap {
     }
 };
 
-// Q fragments of a workgroup's tiles (B operands of S^T = K Q^T), staged
-// through LDS before the first chunk is dequantised there: lane (col, grp)
-// of tile t ends up with query row 16*t + col, 8 values per 32-wide block.
-// For Q4_0 the 8 values follow the element order of q4_unpack, for F16 the
-// natural order.
-//
-// The workgroup reads its rows as contiguous 16-byte pieces (a 1 KB span
-// per wave instruction; read straight into fragments, each instruction
-// would gather 32-byte pieces of 16 rows), then each wave gathers its
-// fragments from LDS. A wave runs alone on its SIMD here, so the address
-// arithmetic before the loads is not hidden: one division per thread, then
-// 32-bit offsets stepped row by row into a buffer over the query tensor.
-//
-// load() issues every load of the thread, with no branch around any of
-// them; the caller may issue other loads before store(), which waits only
-// for these (loads complete in issue order). Rows past the last query row
-// fall past the end of the tensor and read as zero; every slot a lane reads
-// in store() is written first (by the group's rows, the next group's rows or
-// those zeros), and a padding row's partial state is never written. `lds`
-// must be free when store() starts; it is free again on return (after a
-// barrier).
 // Byte offset of query row r of KV head gkv (node r / G, head gkv*G + r % G)
 // in a [node][H_q][D] fp16 tensor, stepped `rs` rows at a time with one
 // division in all (the row step is at most one carry of the head index).
@@ -288,6 +267,28 @@ struct RowWalk {
     }
 };
 
+// Q fragments of a workgroup's tiles (B operands of S^T = K Q^T), staged
+// through LDS before the first chunk is dequantised there: lane (col, grp)
+// of tile t ends up with query row 16*t + col, 8 values per 32-wide block.
+// For Q4_0 the 8 values follow the element order of q4_unpack, for F16 the
+// natural order.
+//
+// The workgroup reads its rows as contiguous 16-byte pieces (a 1 KB span
+// per wave instruction; read straight into fragments, each instruction
+// would gather 32-byte pieces of 16 rows) and writes them to LDS in the
+// fragments' element order, so that each wave reads a fragment as one
+// 16-byte piece. A wave runs alone on its SIMD here, so the address
+// arithmetic before the loads is not hidden: one division per thread, then
+// 32-bit offsets stepped row by row into a buffer over the query tensor.
+//
+// load() issues every load of the thread, with no branch around any of
+// them; loads the caller issues after it and before store() stay in flight,
+// since store() waits only for these (loads complete in issue order). Rows
+// past the last query row fall past the end of the tensor and read as zero;
+// every slot a lane reads in store() is written first (by the group's rows,
+// the next group's rows or those zeros), and a padding row's partial state
+// is never written. `lds` must be free when store() starts; it is free
+// again on return (after a barrier).
 template <int D, int KVT, int NOWN, int NSH>
 struct QStage {
     static constexpr int NS = NOWN + NSH;
