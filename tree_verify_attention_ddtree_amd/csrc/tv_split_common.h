@@ -174,7 +174,11 @@ struct Stage {
     static constexpr int NB = D / 32;   // 32-wide blocks per row
     static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
     static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
-    static constexpr int VSTR = kChunk + 8;  // V^T row stride in LDS (halves)
+    // V^T row stride in LDS (halves). Q4_0: 160 bytes, an odd multiple of
+    // 32, so that a PV fragment read (16 rows x 4 lane groups of 16 bytes)
+    // meets no bank conflict. F16 keeps 144 bytes, which measured faster
+    // for its kernel (8K context: 29.7 against 30.3 us at 160).
+    static constexpr int VSTR = KVT == TV_KV_Q4_0 ? kChunk + 16 : kChunk + 8;
     static constexpr int KELEMS = kChunk * KSTR;
     static constexpr int VELEMS = D * VSTR;
     static constexpr int ELEMS = KELEMS + VELEMS;

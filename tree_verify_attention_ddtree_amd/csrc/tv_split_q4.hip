@@ -265,12 +265,16 @@ struct Q4Loader {
 
 // Split kernel. Own tiles: each wave holds NOWN query tiles for all D.
 // Shared tiles (the one or two tiles left over when the tile count is not a
-// multiple of four): every wave computes their scores and softmax over the
-// whole chunk (identical in the four waves) but accumulates only its quarter
-// of D, so a shared tile costs a quarter of an own tile's registers. Each
-// wave walks the D-tiles rotated by its index, so that its shared quarter is
-// the first NDT/4 positions of every k-step and every index into the
-// register arrays stays a compile-time constant.
+// multiple of four) are split two ways: wave w scores only key tile w of
+// each chunk (16 of its 64 keys) and accumulates only its quarter of D.
+// The fp16 P of the four key tiles meets in LDS, so each wave's PV sees all
+// 64 keys. The running maximum of a shared tile is common to the waves: a
+// wave whose key tile would move it by more than kTau raises a flag, and
+// when any flag is up every wave takes the largest of the four maxima,
+// rescales and rewrites its P before the PV. Each wave walks the D-tiles
+// rotated by its index, so that its shared quarter is the first NDT/4
+// positions of every k-step and every index into the register arrays stays
+// a compile-time constant.
 template <int D, int NOWN, int NSH, bool MASK>
 __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 {
@@ -282,6 +286,14 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     constexpr int NS = NOWN + NSH;
     static_assert(NS >= 1 && NS <= kMaxSlots, "slots");
     __shared__ __attribute__((aligned(16))) _Float16 lds[2 * St::ELEMS];
+    // shared tiles, by chunk parity: P^T fragments of the chunk
+    // ([k-step][lane], 8 halves), the maximum each wave's key tile was taken
+    // against per row, and the waves' rescale flags
+    constexpr int NSX = NSH > 0 ? NSH : 1;
+    __shared__ __attribute__((aligned(16))) _Float16 psh[2][NSX][2 * 64 * 8];
+    __shared__ float shmax[2][NSX][4][16];
+    __shared__ __attribute__((aligned(16))) int shflag[2][4];
+    __shared__ float shl[NSX][4][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -349,40 +361,61 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         ld.load_v(chunk_row<MASK>(a, c_begin + 1));
     }
 
+    // One barrier per chunk. Without shared tiles it opens the chunk: stage
+    // st has been written, stage st ^ 1 read, by every wave. With shared
+    // tiles it is the one before the PV (below), which orders the same
+    // accesses: K(c+1) is written before it and read after the next one;
+    // V(c+1) is written after it, V(c-1) was read before it. The exchange
+    // buffers alternate with the stages, so a wave writing chunk c+1's
+    // never meets one still reading chunk c's.
+    if constexpr (NSH > 0) __syncthreads();
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int st = (int)((c - c_begin) & 1);
         const _Float16 *ks = lds + st * St::ELEMS;
         const _Float16 *vt = ks + St::KELEMS;
         _Float16 *ks_n = lds + (st ^ 1) * St::ELEMS;
         _Float16 *vt_n = ks_n + St::KELEMS;
-        __syncthreads();
+        if constexpr (NSH == 0) __syncthreads();
 
-        // ---- S^T = K Q^T for every slot and the 4 key tiles of the chunk,
-        // with the K dequantisation of chunk c+1 in between. K fragments
-        // stream through a 4-entry ring, three ahead of use (an LDS read under
-        // load takes longer than the 2 x 3 MFMAs a two-ahead ring covers).
+        // ---- S^T = K Q^T for the own slots over the 4 key tiles of the
+        // chunk and for the shared slots over key tile w, with the K
+        // dequantisation of chunk c+1 in between. K fragments stream through
+        // a 4-entry ring, three ahead of use (an LDS read under load takes
+        // longer than the 2 x 3 MFMAs a two-ahead ring covers); the shared
+        // slots' fragments of key tile w through a 2-entry ring, one block
+        // ahead.
         constexpr int TOT = NB * 4;
-        f4 sacc[NS][4];
+        f4 sacc[NOWN > 0 ? NOWN : 1][4];
+        f4 ssh[NSX];
 #pragma unroll
-        for (int k = 0; k < NS; ++k)
+        for (int k = 0; k < NOWN; ++k)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) sacc[k][kt] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
         auto kfrag = [&](int i) -> h8 {
             const int bb = i / 4, kt = i % 4;
             return *(const h8 *)(ks + (16 * kt + col) * St::KSTR + 32 * bb + 8 * grp);
         };
-        h8 kr[4];
+        const _Float16 *kwb = ks + (16 * w + col) * St::KSTR + 8 * grp;
+        h8 kr[4], kw[2];
         kr[0] = kfrag(0);
         kr[1] = kfrag(1);
         kr[2] = kfrag(2);
+        if constexpr (NSH > 0) kw[0] = *(const h8 *)kwb;
 #pragma unroll
         for (int i = 0; i < TOT; ++i) {
             if (i + 3 < TOT) kr[(i + 3) % 4] = kfrag(i + 3);
             const int bb = i / 4, kt = i % 4;
+            if constexpr (NSH > 0)
+                if (kt == 0 && bb + 1 < NB) kw[(bb + 1) & 1] = *(const h8 *)(kwb + 32 * (bb + 1));
 #pragma unroll
-            for (int k = 0; k < NS; ++k)
+            for (int k = 0; k < NOWN; ++k)
                 sacc[k][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[i % 4], qf[k][bb], sacc[k][kt], 0, 0, 0);
             if (kt == 3) {
+#pragma unroll
+                for (int u = 0; u < NSH; ++u)
+                    ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kw[bb & 1], qf[NOWN + u][bb], ssh[u], 0, 0, 0);
                 ld.k_piece(bb, ks_n, magic);
                 TV_SCHED_FENCE();
             }
@@ -393,18 +426,58 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 #pragma unroll
                 for (int k = 0; k < NS; ++k) {
                     const int thr = masked_keys(a, c, row_skip(a, tile[k], tm.t_end, col));
+                    if (k < NOWN) {
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt) mask_tile(sacc[k][kt], kt, grp, thr);
+                        for (int kt = 0; kt < 4; ++kt) mask_tile(sacc[k < NOWN ? k : 0][kt], kt, grp, thr);
+                    } else {
+                        mask_tile(ssh[k >= NOWN ? k - NOWN : 0], w, grp, thr);
+                    }
                 }
             }
         }
 
-        // ---- running maxima (trees: the VALU's dependent-issue latency is
-        // long), one wave-uniform branch for the rare rescale of all slots
-        float mnew[NS];
+        // ---- shared slots: this wave's P^T quarter goes into the fragments
+        // of k-step w / 2 (elements 4 (w & 1) .. + 3), with the maximum it was
+        // taken against and the wave's rescale flag. That maximum is the
+        // common running maximum, or, when some row of the key tile exceeds
+        // it by more than kTau (the flag), the larger of the two per row, so
+        // that no P exceeds 2^kTau. The flags are read after the barrier below.
+        float mnew_sh[NSX], mown[NSX];
+        h2 psv[NSX][2];
+        if constexpr (NSH > 0) {
+            bool need_sh = false;
+#pragma unroll
+            for (int u = 0; u < NSH; ++u) {
+                const float t = fmaxf(fmaxf(ssh[u][0], ssh[u][1]), fmaxf(ssh[u][2], ssh[u][3]));
+                const float ml = xmax_16_32(t) * a.c;
+                need_sh = need_sh || (ml > m[NOWN + u] + kTau);
+                mnew_sh[u] = ml;
+            }
+            const bool flag = __builtin_amdgcn_ballot_w64(need_sh) != 0;
+#pragma unroll
+            for (int u = 0; u < NSH; ++u) {
+                const float mw = flag ? fmaxf(m[NOWN + u], mnew_sh[u]) : m[NOWN + u];
+                mown[u] = mw;
+                psv[u][0] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][0], a.c, -mw)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][1], a.c, -mw)));
+                psv[u][1] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][2], a.c, -mw)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][3], a.c, -mw)));
+                h4 p4;
+                p4.s01 = psv[u][0];
+                p4.s23 = psv[u][1];
+                *(h4 *)(&psh[st][u][0] + ((w >> 1) * 64 + lane) * 8 + 4 * (w & 1)) = p4;
+                if (grp == 0) shmax[st][u][w][col] = mw;
+            }
+            if (lane == 0) shflag[st][w] = flag;
+        }
+
+        // ---- running maxima of the own slots (trees: the VALU's
+        // dependent-issue latency is long), one wave-uniform branch for the
+        // rare rescale
+        float mnew[NOWN > 0 ? NOWN : 1];
         bool need = false;
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
+        for (int k = 0; k < NOWN; ++k) {
             float t[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
@@ -414,23 +487,18 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         }
         if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-            for (int k = 0; k < NS; ++k) {
+            for (int k = 0; k < NOWN; ++k) {
                 const float mm = fmaxf(m[k], mnew[k]);
                 const float f = __builtin_amdgcn_exp2f(m[k] - mm);
                 l[k] *= f;
                 m[k] = mm;
-                if (k < NOWN) {
 #pragma unroll
-                    for (int j = 0; j < NDT; ++j) o[k < NOWN ? k : 0][j] *= f;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < NDQ; ++j) osh[k >= NOWN ? k - NOWN : 0][j] *= f;
-                }
+                for (int j = 0; j < NDT; ++j) o[k][j] *= f;
             }
         }
 
         // ---- fp16 P^T fragments; k-step kk covers key tiles 2kk, 2kk+1
-        h8 pf[NS][2];
+        h8 pf[NOWN > 0 ? NOWN : 1][2];
         auto make_p = [&](int k, int kk) {
             h2 p[4];
 #pragma unroll
@@ -448,7 +516,56 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
             pf[k][kk] = fr;
         };
 #pragma unroll
-        for (int k = 0; k < NS; ++k) make_p(k, 0);
+        for (int k = 0; k < NOWN; ++k) make_p(k, 0);
+
+        // ---- shared slots: once every wave's P quarter is in LDS, all waves
+        // read the same full P^T fragments. If any wave raised its flag, the
+        // new running maximum is the largest of the four maxima the quarters
+        // were taken against, and each quarter is scaled to it in fp16 (a
+        // factor of at most 1); all waves see the same flags and values, so
+        // they keep identical states. Each wave sums its own key tile's P as
+        // used into its row sums; the four waves' sums are added at the end.
+        h8 pfs[NSX][2];
+        if constexpr (NSH > 0) {
+            __syncthreads();
+            const u4v fl = *(const u4v *)shflag[st];
+#pragma unroll
+            for (int u = 0; u < NSH; ++u) {
+                pfs[u][0] = *(const h8 *)(&psh[st][u][0] + lane * 8);
+                pfs[u][1] = *(const h8 *)(&psh[st][u][0] + (64 + lane) * 8);
+            }
+            if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+#pragma unroll
+                for (int u = 0; u < NSH; ++u) {
+                    const float m0 = m[NOWN + u];
+                    const float mw[4] = {shmax[st][u][0][col], shmax[st][u][1][col], shmax[st][u][2][col],
+                                         shmax[st][u][3][col]};
+                    const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+                    const float g = __builtin_amdgcn_exp2f(m0 - mm);
+                    l[NOWN + u] *= g;
+                    m[NOWN + u] = mm;
+#pragma unroll
+                    for (int j = 0; j < NDQ; ++j) osh[u][j] *= g;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const h2 f = pk_rtz(__builtin_amdgcn_exp2f(mw[2 * kk] - mm),
+                                            __builtin_amdgcn_exp2f(mw[2 * kk + 1] - mm));
+                        const h2 fa = {f.x, f.x}, fb = {f.y, f.y};
+                        pfs[u][kk].s01 *= fa;
+                        pfs[u][kk].s23 *= fa;
+                        pfs[u][kk].s45 *= fb;
+                        pfs[u][kk].s67 *= fb;
+                    }
+                    // the same fp16 products as this wave's quarter above
+                    const h2 fo = pk_rtz(__builtin_amdgcn_exp2f(mown[u] - mm), 0.f);
+                    const h2 fo2 = {fo.x, fo.x};
+                    psv[u][0] *= fo2;
+                    psv[u][1] *= fo2;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NSH; ++u) l[NOWN + u] += add_pair(psv[u][0], add_pair(psv[u][1], 0.f));
+        }
 
         // ---- O^T += V^T P^T. k-step 0 runs while the P of k-step 1 is
         // computed; k-step 1 runs while V(c+1) is dequantised.
@@ -479,12 +596,12 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
             if (j < NDQ) {
 #pragma unroll
                 for (int u = 0; u < NSH; ++u)
-                    osh[u][j < NDQ ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 4], pf[NOWN + u][kk],
+                    osh[u][j < NDQ ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[i % 4], pfs[u][kk],
                                                                                    osh[u][j < NDQ ? j : 0], 0, 0, 0);
             }
             if (i == 1) {
 #pragma unroll
-                for (int k = 0; k < NS; ++k) make_p(k, 1);
+                for (int k = 0; k < NOWN; ++k) make_p(k, 1);
             }
             if (kk == 1 && (j + 1) % VSTEP == 0) {
                 ld.v_piece((j + 1) / VSTEP - 1, vt_n, magic);
@@ -506,10 +623,21 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH>;
     const __amdgpu_buffer_rsrc_t rwo = raw_rsrc(a.ws_o + (int64_t)split * a.NR * D, (u32)a.NR * (u32)(2 * D));
     const __amdgpu_buffer_rsrc_t rwm = raw_rsrc(a.ws_m + (int64_t)split * a.NR, (u32)a.NR * 4u);
+#pragma unroll
+    for (int u = 0; u < NSH; ++u) {
+        const float lw = wave_sum_16_32(l[NOWN + u]);
+        if (grp == 0) shl[u][w][col] = lw;
+    }
     __syncthreads();  // every wave is done with the last stage
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-        const float lt = wave_sum_16_32(l[k]);
+        float lt;
+        if (k < NOWN) {
+            lt = wave_sum_16_32(l[k]);
+        } else {
+            const int u = k >= NOWN ? k - NOWN : 0;
+            lt = ((shl[u][0][col] + shl[u][1][col]) + shl[u][2][col]) + shl[u][3][col];
+        }
         const int rl = 16 * (tile[k] - tm.t0) + col;
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
         _Float16 *orow = lds + rl * QS::QSTR + 4 * grp;
