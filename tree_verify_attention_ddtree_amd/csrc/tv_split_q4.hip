@@ -522,7 +522,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         // read the same full P^T fragments. If any wave raised its flag, the
         // new running maximum is the largest of the four maxima the quarters
         // were taken against, and each quarter is scaled to it in fp16 (a
-        // factor of at most 1); all waves see the same flags and values, so
+        // factor of at most 1, rounded to nearest, as the products are); all
+        // waves see the same flags and values, so
         // they keep identical states. Each wave sums its own key tile's P as
         // used into its row sums; the four waves' sums are added at the end.
         h8 pfs[NSX][2];
@@ -548,8 +549,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                     for (int j = 0; j < NDQ; ++j) osh[u][j] *= g;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        const h2 f = pk_rtz(__builtin_amdgcn_exp2f(mw[2 * kk] - mm),
-                                            __builtin_amdgcn_exp2f(mw[2 * kk + 1] - mm));
+                        const h2 f = {(_Float16)__builtin_amdgcn_exp2f(mw[2 * kk] - mm),
+                                      (_Float16)__builtin_amdgcn_exp2f(mw[2 * kk + 1] - mm)};
                         const h2 fa = {f.x, f.x}, fb = {f.y, f.y};
                         pfs[u][kk].s01 *= fa;
                         pfs[u][kk].s23 *= fa;
@@ -557,8 +558,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                         pfs[u][kk].s67 *= fb;
                     }
                     // the same fp16 products as this wave's quarter above
-                    const h2 fo = pk_rtz(__builtin_amdgcn_exp2f(mown[u] - mm), 0.f);
-                    const h2 fo2 = {fo.x, fo.x};
+                    const _Float16 fo = (_Float16)__builtin_amdgcn_exp2f(mown[u] - mm);
+                    const h2 fo2 = {fo, fo};
                     psv[u][0] *= fo2;
                     psv[u][1] *= fo2;
                 }
