@@ -131,10 +131,14 @@ struct Q4Loader {
 
     // Every row of a chunk is a cache row (a window's remainder is either
     // read as the chunk that ends at the window's end or left to the merge
-    // kernel), so no bounds checks beyond the descriptor's.
-    __device__ __forceinline__ void load_k(int64_t chunk_row)
+    // kernel), so no bounds checks beyond the descriptor's. A chunk past the
+    // split's end (valid false) gets an empty descriptor: its loads return
+    // zeros without touching memory. The loads stay unconditional, so every
+    // path through the loop has the same loads in flight and each wait
+    // counts only the loads it needs.
+    __device__ __forceinline__ void load_k(int64_t chunk_row, bool valid)
     {
-        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(kbase + chunk_row * tok_stride, chunk_bytes);
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(kbase + chunk_row * tok_stride, valid ? chunk_bytes : 0u);
         if constexpr (Sh::HB == 4) {
             // blocks 2u and 2u+1: 36 contiguous bytes from a 4-byte aligned start
             const int so = 36 * u;
@@ -164,9 +168,9 @@ struct Q4Loader {
         }
     }
 
-    __device__ __forceinline__ void load_v(int64_t chunk_row)
+    __device__ __forceinline__ void load_v(int64_t chunk_row, bool valid)
     {
-        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(vbase + chunk_row * tok_stride, chunk_bytes);
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(vbase + chunk_row * tok_stride, valid ? chunk_bytes : 0u);
 #pragma unroll
         for (int q = 0; q < Sh::NKV; ++q) {
             const int so = (int)(q * tok_stride);
@@ -323,8 +327,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     qs.load(a, gkv, tm.t0, tid);
     L ld;
     ld.init(a, gkv, tid);
-    ld.load_k(chunk_row<MASK>(a, c_begin));
-    ld.load_v(chunk_row<MASK>(a, c_begin));
+    ld.load_k(chunk_row<MASK>(a, c_begin), true);
+    ld.load_v(chunk_row<MASK>(a, c_begin), true);
 
     h8 qf[NS][NB];
     qs.store(tm.t0, tile, tid, col, grp, lds, qf);
@@ -356,10 +360,8 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     for (int j = 0; j < NB; ++j) ld.k_piece(j, lds, magic);
 #pragma unroll
     for (int p = 0; p < L::V_PIECES; ++p) ld.v_piece(p, lds + St::KELEMS, magic);
-    if (c_begin + 1 < c_end) {
-        ld.load_k(chunk_row<MASK>(a, c_begin + 1));
-        ld.load_v(chunk_row<MASK>(a, c_begin + 1));
-    }
+    ld.load_k(chunk_row<MASK>(a, c_begin + 1), c_begin + 1 < c_end);
+    ld.load_v(chunk_row<MASK>(a, c_begin + 1), c_begin + 1 < c_end);
 
     // One barrier per chunk. Without shared tiles it opens the chunk: stage
     // st has been written, stage st ^ 1 read, by every wave. With shared
@@ -420,7 +422,7 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                 TV_SCHED_FENCE();
             }
         }
-        if (c + 2 < c_end) ld.load_k(chunk_row<MASK>(a, c + 2));
+        ld.load_k(chunk_row<MASK>(a, c + 2), c + 2 < c_end);
         if constexpr (MASK) {
             if (chunk_masked(a, c)) {
 #pragma unroll
@@ -609,7 +611,7 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
                 TV_SCHED_FENCE();
             }
         }
-        if (c + 2 < c_end) ld.load_v(chunk_row<MASK>(a, c + 2));
+        ld.load_v(chunk_row<MASK>(a, c + 2), c + 2 < c_end);
     }
 
     // ---- partial states: own tiles by every wave; shared tiles by every
