@@ -169,16 +169,17 @@ __device__ __forceinline__ int vpos(int kappa)
     return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool WIDE_V = false>
 struct Stage {
     static constexpr int NB = D / 32;   // 32-wide blocks per row
     static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
     static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
-    // V^T row stride in LDS (halves). Q4_0: 160 bytes, an odd multiple of
-    // 32, so that a PV fragment read (16 rows x 4 lane groups of 16 bytes)
-    // meets no bank conflict. F16 keeps 144 bytes, which measured faster
-    // for its kernel (8K context: 29.7 against 30.3 us at 160).
-    static constexpr int VSTR = KVT == TV_KV_Q4_0 ? kChunk + 16 : kChunk + 8;
+    // V^T row stride in LDS (halves): 144 bytes, or with WIDE_V 160 bytes,
+    // an odd multiple of 32, at which a PV fragment read (16 rows x 4 lane
+    // groups of 16 bytes) meets no bank conflict. The Q4_0 kernels with
+    // shared tiles take the wide stride (128K context: 105.5 against 107.8
+    // us); those without, and the F16 kernels, measured faster at 144 bytes.
+    static constexpr int VSTR = WIDE_V ? kChunk + 16 : kChunk + 8;
     static constexpr int KELEMS = kChunk * KSTR;
     static constexpr int VELEMS = D * VSTR;
     static constexpr int ELEMS = KELEMS + VELEMS;
