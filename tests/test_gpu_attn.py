@@ -204,6 +204,35 @@ def test_peaky_scores_force_rescaling():
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("n_nodes", [2, 4, 23])
+def test_peaky_scores_force_rescaling_q4_0(n_nodes):
+    """Q4_0 keys whose block scales rise 30-fold over every 256 rows (four
+    64-key chunks; a split here covers four or five): the running maxima
+    move by far more than the lazy-rescale threshold in later chunks of a
+    split too, not only in its first. 2 and 4 nodes give one and two
+    query tiles (shared tiles only), 23 nodes two own tiles and a shared one
+    per wave, so both rescale paths of the Q4_0 split kernel run, the shared
+    tiles' one with the waves' P quarters taken against different maxima.
+    The key scales are rounded to powers of two, so that the dequantised
+    keys are exact in fp16: at scores this large (up to ~55 in log2 units)
+    the one rounding of an ordinary scale times a code moves a score by
+    more than the tolerance allows (row errors 6e-3 to 8e-3 measured, with
+    or without the rescaling), which this test is not about."""
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=20000, n_nodes=n_nodes))
+    inp["q"] = (inp["q"].astype(np.float32) * 16).astype(np.float16)
+    c = inp["k_cache"].copy()
+    blocks = c.reshape(c.shape[0], c.shape[1], -1, 18)
+    sc = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float32)
+    ramp = (0.2 + 5.8 * (np.arange(c.shape[1]) % 256) / 255.0).astype(np.float32)[None, :, None]
+    scr = sc * ramp
+    p2 = np.exp2(np.round(np.log2(np.where(scr > 0, scr, 1.0))))
+    sc16 = np.where(scr > 0, p2, 0.0).astype(np.float16)
+    blocks[..., 0:2] = sc16[..., None].view(np.uint8).reshape(sc16.shape + (2,))
+    inp["k_cache"] = c
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
 def test_deterministic():
     inp = synth.attn_inputs(**synth.WORKLOADS["27b"])
     a, b = gpu_attn(inp, repeat=2)
