@@ -6,11 +6,12 @@
 // shared), but the dequantisation of chunk c+1 is interleaved with the MFMAs
 // of chunk c so that the VALU work runs in the shadow of the matrix cores:
 //
-//   iteration c:  barrier
+//   iteration c:  barrier (without shared tiles)
 //                 S^T(c) = K Q^T MFMAs   + dequantise K(c+1) into the other
 //                                          LDS stage, one code dword per block
 //                 load raw K(c+2)
-//                 online softmax(c)
+//                 online softmax(c); shared tiles' P quarters to LDS
+//                 barrier (with shared tiles), P quarters read back
 //                 O^T += V^T P^T MFMAs   + dequantise V(c+1)
 //                 load raw V(c+2)
 //
