@@ -60,13 +60,13 @@ static int check_desc(const tv_attn_desc *d)
 
 // Tile roles for T tiles cut into RG row groups; false when a group needs
 // more tile slots per wave than the kernels have.
-static bool rows_for_groups(int T, int RG, RowPlan *rp)
+static bool rows_for_groups(int T, int RG, bool three_shared, RowPlan *rp)
 {
     int nown = 0, nsh = 0;
     for (int g = 0; g < RG; ++g) {
         const int Tg = T / RG + (g < T % RG ? 1 : 0);
         int o, s;
-        group_roles(Tg, &o, &s);
+        group_roles(Tg, &o, &s, three_shared);
         nown = o > nown ? o : nown;
         nsh = s > nsh ? s : nsh;
     }
@@ -78,11 +78,11 @@ static bool rows_for_groups(int T, int RG, RowPlan *rp)
     return true;
 }
 
-static int plan_rows(int M, RowPlan *rp)
+static int plan_rows(int M, bool three_shared, RowPlan *rp)
 {
     const int T = (M + 15) / 16;
     for (int RG = 1; RG <= T; ++RG)
-        if (rows_for_groups(T, RG, rp)) return TV_OK;
+        if (rows_for_groups(T, RG, three_shared, rp)) return TV_OK;
     return TV_E_SHAPE;
 }
 
@@ -90,7 +90,9 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
 {
     const int G = d->n_q_heads / d->n_kv_heads;
     const int M = G * d->n_nodes;
-    int rc = plan_rows(M, &out->rows);
+    // the Q4_0 kernels have an all-shared layout for three tiles
+    const bool three_shared = d->kv_type == TV_KV_Q4_0;
+    int rc = plan_rows(M, three_shared, &out->rows);
     if (rc) return rc;
     out->s0 = (d->window > 0 && d->n_ctx > d->window) ? d->n_ctx - d->window : 0;
     out->R = d->n_ctx - out->s0;
@@ -162,7 +164,7 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     for (int RG = out->rows.groups + 1; RG <= out->rows.tiles; ++RG) {
         if ((int64_t)out->S * d->n_kv_heads * RG > n_cu) break;
         RowPlan rp;
-        if (rows_for_groups(out->rows.tiles, RG, &rp)) out->rows = rp;
+        if (rows_for_groups(out->rows.tiles, RG, three_shared, &rp)) out->rows = rp;
     }
     return TV_OK;
 }

@@ -25,10 +25,15 @@ struct RowPlan {
 // Per-group tile roles: a group of Tg tiles gives every wave Tg/4 own tiles;
 // of the Tg%4 left over, 1 or 2 are shared (each split by keys over the four
 // waves) and 3 become one more own tile for waves 0..2.
-inline void group_roles(int Tg, int *own_max, int *sh)
+inline void group_roles(int Tg, int *own_max, int *sh, bool three_shared)
 {
     const int a = Tg / 4, r = Tg % 4;
-    if (r == 3) {
+    if (r == 3 && a == 0 && three_shared) {
+        // three tiles: all shared (each wave scores one key tile of each)
+        // rather than one own tile for three waves and none for the fourth
+        *own_max = 0;
+        *sh = 3;
+    } else if (r == 3) {
         *own_max = a + 1;
         *sh = 0;
     } else {

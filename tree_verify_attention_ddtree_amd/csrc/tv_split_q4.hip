@@ -300,7 +300,6 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     __shared__ __attribute__((aligned(16))) _Float16 psh[2][NSX][2 * 64 * 8];
     __shared__ float shmax[2][NSX][4][16];
     __shared__ __attribute__((aligned(16))) int shflag[2][4];
-    __shared__ float shl[NSX][4][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -631,6 +630,10 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
     using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH>;
     const __amdgpu_buffer_rsrc_t rwo = raw_rsrc(a.ws_o + (int64_t)split * a.NR * D, (u32)a.NR * (u32)(2 * D));
     const __amdgpu_buffer_rsrc_t rwm = raw_rsrc(a.ws_m + (int64_t)split * a.NR, (u32)a.NR * 4u);
+    // the shared tiles' row sums meet in the maxima buffer of the parity
+    // the last chunk did not use: every wave read it before the last
+    // chunk's barrier
+    float(*shl)[4][16] = shmax[((int)(c_end - c_begin) & 1)];
 #pragma unroll
     for (int u = 0; u < NSH; ++u) {
         const float lw = wave_sum_16_32(l[NOWN + u]);
@@ -686,8 +689,8 @@ static split_fn pick_q4(int nown, int nsh)
 {
 #define TV_CASE(O, S) \
     if (nown == O && nsh == S) return split_q4_kernel<D, O, S, MASK>;
-    TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
-    TV_CASE(3, 0)
+    TV_CASE(0, 1) TV_CASE(0, 2) TV_CASE(0, 3) TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0)
+    TV_CASE(2, 1) TV_CASE(3, 0)
 #undef TV_CASE
     return nullptr;
 }
