@@ -478,14 +478,14 @@ __device__ __forceinline__ void cache_values(const uint8_t *row, int kv_type, in
 }
 
 // One workgroup of 256 threads per output row (node i, query head h), in
-// three rounds of independent loads:
+// three steps of independent loads:
 //   1. thread (split group sg, d-octet dq) loads the partial states of its
 //      splits s = sg, sg + NGR, ... and folds them against their own maximum;
 //      at the same time the threads score the row's extra keys (its tree
 //      ancestors, then the window's tail rows), KL lanes per key;
 //   2. the maximum over splits and extra keys;
 //   3. the extra keys' V rows are spread over the split groups (the first
-//      VPF of each group are loaded during round 1, as they do not depend on
+//      VPF of each group are loaded during step 1, as they do not depend on
 //      the scores); the groups' sums meet in LDS.
 // A split's weight is 2^(lse_s - m*) with lse_s the log2 of its softmax
 // denominator, an extra key's 2^(score - m*); the output is the weighted sum
@@ -562,7 +562,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
     if (kk0 < na) ktr = *(const hk *)(a.k_tree + tree_row(kk0) * D + kl * KPT);
     else if (kk0 < nk) cache_k(kk0, kc0);
 
-    // round 1a's loads for this thread's first SMAX splits, behind those
+    // step 1a's loads for this thread's first SMAX splits, behind those
     // above (the scores need their loads sooner); no branch around a load: a
     // split past the last reads split 0, and the fold gives it no weight
     float mv[SMAX];
@@ -575,7 +575,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
         ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
     }
 
-    // ---- round 1a: this thread's splits, folded against their maximum
+    // ---- step 1a: this thread's splits, folded against their maximum
     float ms = kNegBig;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
@@ -607,7 +607,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
         }
         ms = mb;
     }
-    // ---- round 1b: scores of the extra keys (ancestors, then tail rows)
+    // ---- step 1b: scores of the extra keys (ancestors, then tail rows)
     float mk = -INFINITY;
     {
         float qv[KPT];
@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
             }
         }
     }
-    // ---- round 2: maxima
+    // ---- step 2: maxima
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off));
     if (lane == 0) red_k[w] = mk;
@@ -655,7 +655,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] *= r;
     }
-    // ---- round 3: the extra keys' V rows, spread over the split groups
+    // ---- step 3: the extra keys' V rows, spread over the split groups
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
         const int kk = sg + NGR * j;
