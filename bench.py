@@ -106,7 +106,8 @@ def copy_calibration(nbytes, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "the step is measured on one GPU (the library runs one GPU's "
+                                   "share of a sharded step); run with --gpus 1"}))
         sys.exit(2)
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, args.steps)
