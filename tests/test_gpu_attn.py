@@ -128,6 +128,17 @@ def test_tile_layouts(Hq, Hkv, n, D, kv):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("Hq,Hkv,n,D", [(6, 1, 8, 256), (6, 1, 7, 64), (2, 1, 21, 128), (8, 1, 16, 256)])
+def test_tile_layouts_whole_chunks(Hq, Hkv, n, D):
+    """Q4_0 layouts on a cache of whole 64-row chunks (the unmasked split
+    kernels; the 700-row cases above take the masked ones): three shared
+    tiles (M = 48, 42, 42) and eight own tiles (M = 128)."""
+    inp = synth.attn_inputs(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_ctx=4096, n_nodes=n,
+                            depth_cap=16, seed=2000 + Hq * 7 + n)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("n_ctx", [0, 1, 5, 63, 64, 65, 127, 255, 1000, 4097])
 def test_ragged_and_empty_caches(n_ctx):
     w = dict(synth.WORKLOADS["27b"], n_ctx=max(n_ctx, 1))
