@@ -136,6 +136,46 @@ typedef struct tv_attn_ptrs {
  */
 TV_API size_t tv_attn_workspace_bytes(const tv_attn_desc *d);
 
+/* Split kernels a plan may launch (tv_attn_plan_info.kernel). */
+#define TV_SPLIT_NONE 0  /* no whole 64-row chunk: the merge kernel scores every key */
+#define TV_SPLIT_F16 1   /* F16 cache, one wave per SIMD */
+#define TV_SPLIT_Q4_0 2  /* Q4_0 cache, one wave per SIMD, dequantisation interleaved with the MFMAs */
+
+/*
+ * How tree_verify_attn would run `d` on a device with `n_cu` compute units
+ * (n_cu <= 0: the current device's count, which needs the HIP runtime). A
+ * host-only query: it checks `d` like tree_verify_attn, launches nothing and
+ * touches no device memory, so callers and tests can see the split plan
+ * (and size the workspace) without a GPU.
+ *
+ * splits        key-range splits per (KV head, row group); 0 when no whole
+ *               64-row chunk is left for the split kernel
+ * row_groups    groups the G * n_nodes packed query rows of a KV head are cut
+ *               into (16-row tiles; each group is one workgroup per split)
+ * own_tiles     most 16-row tiles one wave holds for all keys
+ * shared_tiles  tiles whose keys are divided among the waves
+ * masked        1 when the split kernel masks keys (a window end or start
+ *               that is not on a chunk boundary)
+ * kernel        TV_SPLIT_*
+ * chunks        64-row chunks the split kernel covers per KV head
+ * merge_rows    cache rows per node the merge kernel scores one by one
+ * workspace_bytes  tv_attn_workspace_bytes for that device
+ * Returns TV_OK or the TV_E_* code tree_verify_attn would return for `d`.
+ */
+typedef struct tv_attn_plan_info {
+    int32_t splits;
+    int32_t row_groups;
+    int32_t own_tiles;
+    int32_t shared_tiles;
+    int32_t masked;
+    int32_t kernel;
+    int64_t chunks;
+    int64_t merge_rows;
+    uint64_t workspace_bytes;
+} tv_attn_plan_info;
+
+TV_API int tv_attn_plan(const tv_attn_desc *d, int32_t n_cu, tv_attn_plan_info *out);
+
 /*
  * One layer of tree-verify attention, asynchronous on `stream`:
  *   out[i][h] = softmax over keys k of scale * q[i][h] . k, applied to the

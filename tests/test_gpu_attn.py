@@ -128,6 +128,74 @@ def test_tile_layouts(Hq, Hkv, n, D, kv):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+@pytest.mark.parametrize("n,layout", [(8, {"q4_0": (0, 3), "f16": (1, 0)}), (20, {"q4_0": (2, 0), "f16": (2, 0)}),
+                                      (30, {"q4_0": (3, 0), "f16": (3, 0)}), (23, {"q4_0": (2, 1), "f16": (2, 1)})])
+def test_tile_layouts_27b_heads(n, layout, kv):
+    """The 27B head layout (24 q / 4 kv heads) over 64 whole chunks per KV
+    head: 8, 20, 30 and 23 nodes make 3, 8, 12 and 9 query tiles. The plan
+    the library reports for this device is asserted first, so each case is
+    known to run the tile layout it is named for (one row group, unmasked)."""
+    import tree_verify_attention_ddtree_amd as tv
+    inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=4096, n_nodes=n, depth_cap=16,
+                            seed=3000 + n, kv=kv)
+    kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+    row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
+    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, 4096, 0, inp["scale"], row, row * 4096)
+    plan = tv.tv_attn_plan(desc)
+    assert (plan["own_tiles"], plan["shared_tiles"]) == layout[kv], plan
+    assert plan["row_groups"] == 1 and plan["masked"] == 0, plan
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+@pytest.mark.parametrize("n_ctx", [0, 5, 63])
+def test_no_workspace_without_splits(kv, n_ctx):
+    """Fewer than 64 cache rows: no split runs, the workspace is 0 bytes and
+    is passed as NULL (and so are the caches when they are empty)."""
+    import torch
+
+    import tree_verify_attention_ddtree_amd as tv
+    w = dict(synth.WORKLOADS["27b"], n_ctx=max(n_ctx, 1))
+    inp = synth.attn_inputs(**w, kv=kv)
+    inp["k_cache"] = inp["k_cache"][:, :n_ctx]
+    inp["v_cache"] = inp["v_cache"][:, :n_ctx]
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).cuda() for k in ("q", "k_tree", "v_tree")}
+    kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+    row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
+    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, n_ctx, 0, inp["scale"], row, row * max(n_ctx, 1))
+    assert tv.tv_attn_workspace_bytes(desc) == 0
+    kc = vc = None
+    if n_ctx > 0:
+        kc = torch.from_numpy(np.ascontiguousarray(inp["k_cache"])).cuda()
+        vc = torch.from_numpy(np.ascontiguousarray(inp["v_cache"])).cuda()
+    out = torch.full((23, 24, 256), float("nan"), dtype=torch.float32, device="cuda")
+    tv.tree_verify_attn(desc, kc, vc, t["q"], t["k_tree"], t["v_tree"], out, None, 0)
+    torch.cuda.synchronize()
+    err = rownorm_err(out.cpu().numpy().astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+def test_non_finite_scales_stay_in_their_kv_head():
+    """Q4_0 blocks with +inf, -inf and NaN scales in KV head 1 only (a commit
+    of a row holding +-inf writes such scales): the rows of that head's
+    query heads are unspecified, every other row matches the oracle."""
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=1000))
+    for k, bits in (("k_cache", (0x7C00, 0xFE00)), ("v_cache", (0xFC00, 0x7C00))):
+        c = inp[k].copy()
+        blocks = c.reshape(c.shape[0], c.shape[1], -1, 18)
+        for j, b in enumerate(bits):
+            blocks[1, 100 + 300 * j, 2, 0:2] = np.array([b], np.uint16).view(np.uint8)
+        inp[k] = c
+    got = gpu_attn(inp).astype(np.float64)
+    ref = oracle.attn(inp)
+    keep = [h for h in range(24) if h // 6 != 1]
+    assert np.isfinite(ref[:, keep]).all() and np.isfinite(got[:, keep]).all()
+    err = rownorm_err(got[:, keep], ref[:, keep])
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("Hq,Hkv,n,D", [(6, 1, 8, 256), (6, 1, 7, 64), (2, 1, 21, 128), (8, 1, 16, 256)])
 def test_tile_layouts_whole_chunks(Hq, Hkv, n, D):
     """Q4_0 layouts on a cache of whole 64-row chunks (the unmasked split

@@ -85,14 +85,17 @@ def test_bad_shapes_rejected(L, kw, code):
 
 
 def test_null_and_misaligned_pointers_rejected(L):
+    """Every call here fails a host check, so nothing is launched even where a
+    GPU is visible (the fake pointers are never dereferenced). That an empty
+    cache may be NULL, with no workspace, is checked on the GPU."""
     d, keep = _desc()
     assert _call(L, d, tv.TvAttnPtrs(4096, 4096, None, 4096, 4096, 4096)) == -1
     assert _call(L, d, tv.TvAttnPtrs(None, 4096, 4096, 4096, 4096, 4096)) == -1
     assert _call(L, d, tv.TvAttnPtrs(4096, 4096, 4098, 4096, 4096, 4096)) == -4
     assert _call(L, d, tv.TvAttnPtrs(4104, 4096, 4096, 4096, 4096, 4096)) == -4
-    # an empty cache may be NULL; the call then fails only later, on the device
     d0, keep0 = _desc(n_ctx=0)
-    assert _call(L, d0, tv.TvAttnPtrs(None, None, 4096, 4096, 4096, 4096)) not in (-1, -4)
+    assert _call(L, d0, tv.TvAttnPtrs(None, None, None, 4096, 4096, 4096)) == -1
+    assert _call(L, d0, tv.TvAttnPtrs(None, None, 4096, 4096, 4096, 4100)) == -4
     assert L.tree_verify_attn(None, None, None, 0, None) == -1
 
 
@@ -169,4 +172,64 @@ def test_window_mode_checked(L):
     d.window_mode = 2
     assert _call(L, d) == -1
     d.window_mode = 1
-    assert _call(L, d) not in (-1, -3, -4)  # valid: fails only later, on the device
+    assert tv.tv_attn_plan(d, 256)["splits"] > 0  # valid (host-only query: nothing launched)
+
+
+def test_row_bytes_fit_32_bit_offsets(L):
+    """q, out and each split's workspace block are addressed with 32-bit
+    buffer offsets: n * H_q * 2 * head_dim must stay below 2^31."""
+    parent = tuple([-1] + list(range(63)))
+    d, keep = _desc(parent=parent, Hq=1 << 16, Hkv=1, D=256, ts=144, hs=144 * 256)
+    assert _call(L, d) == -3
+    d, keep = _desc(parent=parent, Hq=(1 << 16) - 4, Hkv=1, D=256, ts=144, hs=144 * 256)
+    assert tv.tv_attn_plan(d, 256)["splits"] >= 1
+    # more than 65535 KV heads do not fit the split grid
+    d, keep = _desc(parent=(-1,), Hq=1 << 16, Hkv=1 << 16, D=64)
+    assert _call(L, d) == -3
+
+
+def _plan(Hq, Hkv, n, D, kv, n_ctx, window=0, window_mode=0, n_cu=256):
+    par = [-1] + [max(0, i - 1) for i in range(1, n)]
+    row = D // 32 * 18 if kv == tv.TV_KV_Q4_0 else 2 * D
+    d, keep = tv.make_desc(par, Hq, Hkv, D, kv, n_ctx, window, 0.0625, row, row * max(n_ctx, 1),
+                           window_mode=window_mode)
+    return tv.tv_attn_plan(d, n_cu)
+
+
+def test_plan_query_layouts():
+    """The 27B head layout (24 q / 4 kv heads) on 256 compute units, 64
+    whole chunks per KV head: 8, 20 and 30 nodes give 3, 8 and 12 query
+    tiles, which the Q4_0 kernels take as three shared tiles, two own tiles
+    per wave and three own tiles per wave, with one row group."""
+    Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
+    p = _plan(24, 4, 8, 256, Q, 4096)
+    assert (p["own_tiles"], p["shared_tiles"], p["row_groups"], p["masked"]) == (0, 3, 1, 0)
+    assert (p["splits"], p["chunks"], p["kernel"]) == (64, 64, tv.TV_SPLIT_Q4_0)
+    p = _plan(24, 4, 8, 256, F, 4096)
+    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16)
+    for kv in (Q, F):
+        p = _plan(24, 4, 20, 256, kv, 4096)
+        assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (2, 0, 1)
+        p = _plan(24, 4, 30, 256, kv, 4096)
+        assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (3, 0, 1)
+    # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits
+    p = _plan(24, 4, 23, 256, Q, 131072)
+    assert (p["own_tiles"], p["shared_tiles"], p["splits"], p["chunks"]) == (2, 1, 64, 2048)
+    assert p["workspace_bytes"] == 64 * 23 * 24 * (2 * 256 + 4)
+    # a 2048-row window: 32 chunks cap the splits, the rows are cut in two groups
+    p = _plan(24, 4, 23, 256, Q, 61440, window=2048)
+    assert (p["splits"], p["row_groups"], p["chunks"]) == (32, 2, 32)
+    # a ragged window end: the masked kernel while splits stay short
+    p = _plan(24, 4, 23, 256, Q, 8192 + 31)
+    assert p["masked"] == 1 and p["merge_rows"] == 0
+    # ... and the merge kernel's rows once they are long
+    p = _plan(24, 4, 23, 256, Q, 131072 + 31)
+    assert p["masked"] == 0 and p["merge_rows"] == 31
+
+
+@pytest.mark.parametrize("n_ctx", [0, 5, 63])
+def test_plan_without_splits_needs_no_workspace(n_ctx):
+    for kv in (tv.TV_KV_Q4_0, tv.TV_KV_F16):
+        p = _plan(24, 4, 23, 256, kv, n_ctx)
+        assert p["splits"] == 0 and p["workspace_bytes"] == 0 and p["kernel"] == tv.TV_SPLIT_NONE
+        assert p["merge_rows"] == n_ctx

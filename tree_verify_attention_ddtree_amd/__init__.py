@@ -54,6 +54,25 @@ class TvAttnPtrs(ctypes.Structure):
     ]
 
 
+class TvAttnPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("splits", ctypes.c_int32),
+        ("row_groups", ctypes.c_int32),
+        ("own_tiles", ctypes.c_int32),
+        ("shared_tiles", ctypes.c_int32),
+        ("masked", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("chunks", ctypes.c_int64),
+        ("merge_rows", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
+TV_SPLIT_NONE = 0
+TV_SPLIT_F16 = 1
+TV_SPLIT_Q4_0 = 2
+
+
 class TvError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
@@ -86,6 +105,8 @@ def lib():
         L.tree_commit_kv.restype = ctypes.c_int
         L.tree_commit_kv_layers.argtypes = [ctypes.POINTER(TvCommitDesc), ctypes.c_int32, P, P, P, P, P, P]
         L.tree_commit_kv_layers.restype = ctypes.c_int
+        L.tv_attn_plan.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.POINTER(TvAttnPlanInfo)]
+        L.tv_attn_plan.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -104,7 +125,7 @@ class TvCommitDesc(ctypes.Structure):
 
 
 EXPORTS = ("tree_verify_attn", "tree_accept", "tree_commit_kv", "tree_commit_kv_layers", "tv_attn_workspace_bytes",
-           "tv_accept_workspace_bytes", "tv_strerror")
+           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan")
 
 
 def tv_strerror(code: int) -> str:
@@ -146,6 +167,17 @@ def cache_strides(cache, kv_type):
 
 def tv_attn_workspace_bytes(desc: TvAttnDesc) -> int:
     return int(lib().tv_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def tv_attn_plan(desc: TvAttnDesc, n_cu: int = 0) -> dict:
+    """The split plan tree_verify_attn would use on a device with n_cu
+    compute units (0: the current device). Host-only; raises TvError for an
+    invalid descriptor."""
+    info = TvAttnPlanInfo()
+    rc = lib().tv_attn_plan(ctypes.byref(desc), int(n_cu), ctypes.byref(info))
+    if rc != TV_OK:
+        raise TvError(rc, "tv_attn_plan")
+    return {name: int(getattr(info, name)) for name, _ in TvAttnPlanInfo._fields_}
 
 
 def tree_verify_attn(desc: TvAttnDesc, k_cache, v_cache, q, k_tree, v_tree, out, workspace=None,

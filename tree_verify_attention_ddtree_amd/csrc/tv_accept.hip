@@ -207,8 +207,12 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
 {
     const int ns = (int)n_slices_for(vocab);
     uint64_t *part = (uint64_t *)ws;
-    hipLaunchKernelGGL(argmax_partial, dim3(ns, n), dim3(kAccThreads), 0, stream, logits, vocab, ns, part);
-    if (hipGetLastError() != hipSuccess) return TV_E_HIP;
+    {
+        void *args[] = {(void *)&logits, (void *)&vocab, (void *)&ns, (void *)&part};
+        if (hipLaunchKernel((const void *)argmax_partial, dim3(ns, n), dim3(kAccThreads), args, 0, stream) !=
+            hipSuccess)
+            return TV_E_HIP;
+    }
     WalkArgs w;
     w.part = part;
     w.argmax_out = argmax_out;
@@ -223,8 +227,9 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
             for (int v = i; v >= 0; v = parent[v]) m |= 1ull << v;
         w.anc[i] = m;
     }
-    hipLaunchKernelGGL(finish_walk, dim3(1), dim3(64), 0, stream, w);
-    if (hipGetLastError() != hipSuccess) return TV_E_HIP;
+    void *wargs[] = {(void *)&w};
+    if (hipLaunchKernel((const void *)finish_walk, dim3(1), dim3(64), wargs, 0, stream) != hipSuccess)
+        return TV_E_HIP;
     return TV_OK;
 }
 

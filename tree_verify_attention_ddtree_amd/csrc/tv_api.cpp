@@ -46,7 +46,11 @@ static int check_desc(const tv_attn_desc *d)
     if (d->n_ctx < 0 || d->window < 0) return TV_E_SHAPE;
     if (d->window_mode != 0 && d->window_mode != 1) return TV_E_ARG;
     if (!(d->scale > 0.0f) || !isfinite(d->scale)) return TV_E_ARG;
-    if ((int64_t)d->n_nodes * d->n_q_heads > (int64_t)1 << 24) return TV_E_SHAPE;
+    // the kernels address q, out and a split's block of the workspace with
+    // 32-bit buffer offsets: n * H_q rows of 2 * head_dim bytes stay below 2^31
+    if ((int64_t)d->n_nodes * d->n_q_heads * 2 * d->head_dim >= ((int64_t)1 << 31)) return TV_E_SHAPE;
+    // grid dimension y of the split kernel
+    if (d->n_kv_heads > 65535) return TV_E_SHAPE;
     if (d->n_ctx > 0) {
         const int64_t row = d->kv_type == TV_KV_Q4_0 ? (int64_t)d->head_dim / 32 * 18 : (int64_t)d->head_dim * 2;
         const int64_t al = d->kv_type == TV_KV_Q4_0 ? 4 : 16;
@@ -226,6 +230,32 @@ size_t tv_attn_workspace_bytes(const tv_attn_desc *d)
 }
 
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int tv_attn_plan(const tv_attn_desc *d, int32_t n_cu, tv_attn_plan_info *out)
+{
+    int rc = tv::check_desc(d);
+    if (rc) return rc;
+    if (!out) return TV_E_ARG;
+    int cu = n_cu;
+    if (cu <= 0) {
+        rc = tv::device_cu_count(&cu);
+        if (rc) return rc;
+    }
+    tv::SplitPlan plan;
+    rc = tv::plan_attn(d, cu, &plan);
+    if (rc) return rc;
+    memset(out, 0, sizeof(*out));
+    out->splits = plan.S;
+    out->row_groups = plan.rows.groups;
+    out->own_tiles = plan.rows.nown;
+    out->shared_tiles = plan.rows.nsh;
+    out->masked = plan.mask;
+    out->kernel = tv::split_kernel_kind(d, plan);
+    out->chunks = plan.S > 0 ? plan.n_chunks : 0;
+    out->merge_rows = plan.head + plan.tail;
+    out->workspace_bytes = tv::attn_ws_bytes(d, plan);
+    return TV_OK;
+}
 
 int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
                      void *stream)

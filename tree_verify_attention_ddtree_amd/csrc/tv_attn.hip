@@ -564,15 +564,19 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a)
 
     // step 1a's loads for this thread's first SMAX splits, behind those
     // above (the scores need their loads sooner); no branch around a load: a
-    // split past the last reads split 0, and the fold gives it no weight
+    // split past the last reads split 0, and the fold gives it no weight.
+    // Without splits (no whole chunk of keys) the workspace may be absent:
+    // nothing is read from it.
     float mv[SMAX];
     h8 ov[SMAX];
+    if (a.S > 0) {
 #pragma unroll
-    for (int k = 0; k < SMAX; ++k) {
-        const int s = sg + NGR * k;
-        const int64_t base = (int64_t)(s < a.S ? s : 0) * a.NR + row;
-        mv[k] = a.ws_m[base];
-        ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
+        for (int k = 0; k < SMAX; ++k) {
+            const int s = sg + NGR * k;
+            const int64_t base = (int64_t)(s < a.S ? s : 0) * a.NR + row;
+            mv[k] = a.ws_m[base];
+            ov[k] = *(const h8 *)(a.ws_o + base * D + 8 * dq);
+        }
     }
 
     // ---- step 1a: this thread's splits, folded against their maximum
@@ -725,6 +729,12 @@ static split_fn pick_split(int D, int kv, int nown, int nsh, bool mask)
     return nullptr;
 }
 
+int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p)
+{
+    if (p.S == 0) return TV_SPLIT_NONE;
+    return d->kv_type == TV_KV_Q4_0 ? TV_SPLIT_Q4_0 : TV_SPLIT_F16;
+}
+
 int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
                 hipStream_t stream)
 {
@@ -827,14 +837,12 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         }
         mg.anc[i] = mk;
     }
-    dim3 mgrid(NR);
-    if (D == 64)
-        hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, stream, mg);
-    else if (D == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, stream, mg);
-    else
-        hipLaunchKernelGGL(merge_kernel<256>, mgrid, dim3(256), 0, stream, mg);
-    if (hipGetLastError() != hipSuccess) return TV_E_HIP;
+    const void *mfn = D == 64 ? (const void *)merge_kernel<64>
+                    : D == 128 ? (const void *)merge_kernel<128> : (const void *)merge_kernel<256>;
+    void *margs[] = {(void *)&mg};
+    // the launch's own status (hipGetLastError would also report, and
+    // clear, an earlier unrelated error)
+    if (hipLaunchKernel(mfn, dim3(NR), dim3(256), margs, 0, stream) != hipSuccess) return TV_E_HIP;
     return TV_OK;
 }
 

@@ -148,8 +148,11 @@ static int launch_commit_t(const tv_commit_desc *d, int n_layers, const int32_t 
         a.k_cache[l] = on ? (uint8_t *)k_cache[l] : nullptr;
         a.v_cache[l] = on ? (uint8_t *)v_cache[l] : nullptr;
     }
-    hipLaunchKernelGGL(commit_kernel<ML>, dim3(d->n_nodes, d->n_kv_heads, n_layers), dim3(64), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? TV_OK : TV_E_HIP;
+    void *args[] = {(void *)&a};
+    return hipLaunchKernel((const void *)commit_kernel<ML>, dim3(d->n_nodes, d->n_kv_heads, n_layers), dim3(64),
+                           args, 0, stream) == hipSuccess
+               ? TV_OK
+               : TV_E_HIP;
 }
 
 int launch_commit(const tv_commit_desc *d, int n_layers, const int32_t *result, const void *const *k_tree,

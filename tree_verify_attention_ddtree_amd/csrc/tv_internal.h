@@ -55,6 +55,8 @@ struct SplitPlan {
 };
 
 int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out);
+// Which split kernel a plan launches (TV_SPLIT_* of tree_verify.h).
+int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p);
 size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p);
 int device_cu_count(int *n_cu);
 

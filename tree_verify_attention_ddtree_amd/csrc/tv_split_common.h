@@ -29,11 +29,7 @@ constexpr u32 kOffNone = 0x80000000u;
 
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
 // loop to its top, which would need a register per fragment.
-#ifndef TV_NO_FENCE
 #define TV_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define TV_SCHED_FENCE()
-#endif
 
 constexpr float kTau = 8.0f;
 constexpr float kNegBig = -1.0e30f;
