@@ -140,6 +140,8 @@ TV_API size_t tv_attn_workspace_bytes(const tv_attn_desc *d);
 #define TV_SPLIT_NONE 0  /* no whole 64-row chunk: the merge kernel scores every key */
 #define TV_SPLIT_F16 1   /* F16 cache, one wave per SIMD */
 #define TV_SPLIT_Q4_0 2  /* Q4_0 cache, one wave per SIMD, dequantisation interleaved with the MFMAs */
+#define TV_SPLIT_Q4_0_WS 3 /* Q4_0 cache, head_dim 256: two waves per SIMD, one running the MFMAs,
+                              the other dequantising the next chunks */
 
 /*
  * How tree_verify_attn would run `d` on a device with `n_cu` compute units

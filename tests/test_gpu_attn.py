@@ -130,12 +130,18 @@ def test_tile_layouts(Hq, Hkv, n, D, kv):
 
 @pytest.mark.parametrize("kv", ["q4_0", "f16"])
 @pytest.mark.parametrize("n,layout", [(8, {"q4_0": (0, 3), "f16": (1, 0)}), (20, {"q4_0": (2, 0), "f16": (2, 0)}),
-                                      (30, {"q4_0": (3, 0), "f16": (3, 0)}), (23, {"q4_0": (2, 1), "f16": (2, 1)})])
+                                      (30, {"q4_0": (3, 0), "f16": (3, 0)}), (23, {"q4_0": (2, 1), "f16": (2, 1)}),
+                                      (10, {"q4_0": (1, 0), "f16": (1, 0)}), (11, {"q4_0": (1, 1), "f16": (1, 1)}),
+                                      (16, {"q4_0": (1, 2), "f16": (1, 2)}), (26, {"q4_0": (1, 1), "f16": (1, 1)})])
 def test_tile_layouts_27b_heads(n, layout, kv):
     """The 27B head layout (24 q / 4 kv heads) over 64 whole chunks per KV
-    head: 8, 20, 30 and 23 nodes make 3, 8, 12 and 9 query tiles. The plan
-    the library reports for this device is asserted first, so each case is
-    known to run the tile layout it is named for (one row group, unmasked)."""
+    head: 8, 20, 30, 23, 10, 11 and 16 nodes make 3, 8, 12, 9, 4, 5 and 6
+    query tiles in one row group; 26 nodes make 10 tiles, cut into two row
+    groups of five (a group holds at most three tile slots per wave). The
+    plan the library reports for this device is asserted first, so each case
+    is known to run the tile layout and split kernel it is named for
+    (unmasked; every layout of the warp-specialised Q4_0 kernel is among
+    them)."""
     import tree_verify_attention_ddtree_amd as tv
     inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=4096, n_nodes=n, depth_cap=16,
                             seed=3000 + n, kv=kv)
@@ -144,7 +150,9 @@ def test_tile_layouts_27b_heads(n, layout, kv):
     desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, 4096, 0, inp["scale"], row, row * 4096)
     plan = tv.tv_attn_plan(desc)
     assert (plan["own_tiles"], plan["shared_tiles"]) == layout[kv], plan
-    assert plan["row_groups"] == 1 and plan["masked"] == 0, plan
+    assert plan["row_groups"] == (2 if n == 26 else 1) and plan["masked"] == 0, plan
+    want = {"f16": tv.TV_SPLIT_F16, "q4_0": tv.TV_SPLIT_Q4_0_WS if layout[kv][0] in (1, 2) else tv.TV_SPLIT_Q4_0}
+    assert plan["kernel"] == want[kv], plan
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
 

@@ -210,18 +210,26 @@ def test_plan_query_layouts():
     for kv in (Q, F):
         p = _plan(24, 4, 20, 256, kv, 4096)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (2, 0, 1)
+        assert p["kernel"] == (tv.TV_SPLIT_Q4_0_WS if kv == Q else tv.TV_SPLIT_F16)
         p = _plan(24, 4, 30, 256, kv, 4096)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (3, 0, 1)
-    # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits
+        # three own tiles per wave do not fit two waves per SIMD
+        assert p["kernel"] == (tv.TV_SPLIT_Q4_0 if kv == Q else tv.TV_SPLIT_F16)
+    # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits,
+    # on the warp-specialised kernel (head_dim 256)
     p = _plan(24, 4, 23, 256, Q, 131072)
     assert (p["own_tiles"], p["shared_tiles"], p["splits"], p["chunks"]) == (2, 1, 64, 2048)
+    assert p["kernel"] == tv.TV_SPLIT_Q4_0_WS
+    # the chain-16 (six tiles: one own, two shared) too; head_dim 128 does not
+    assert _plan(24, 4, 16, 256, Q, 131072)["kernel"] == tv.TV_SPLIT_Q4_0_WS
+    assert _plan(24, 4, 23, 128, Q, 131072)["kernel"] == tv.TV_SPLIT_Q4_0
     assert p["workspace_bytes"] == 64 * 23 * 24 * (2 * 256 + 4)
     # a 2048-row window: 32 chunks cap the splits, the rows are cut in two groups
     p = _plan(24, 4, 23, 256, Q, 61440, window=2048)
     assert (p["splits"], p["row_groups"], p["chunks"]) == (32, 2, 32)
     # a ragged window end: the masked kernel while splits stay short
     p = _plan(24, 4, 23, 256, Q, 8192 + 31)
-    assert p["masked"] == 1 and p["merge_rows"] == 0
+    assert p["masked"] == 1 and p["merge_rows"] == 0 and p["kernel"] == tv.TV_SPLIT_Q4_0
     # ... and the merge kernel's rows once they are long
     p = _plan(24, 4, 23, 256, Q, 131072 + 31)
     assert p["masked"] == 0 and p["merge_rows"] == 31

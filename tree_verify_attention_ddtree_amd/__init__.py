@@ -71,6 +71,7 @@ class TvAttnPlanInfo(ctypes.Structure):
 TV_SPLIT_NONE = 0
 TV_SPLIT_F16 = 1
 TV_SPLIT_Q4_0 = 2
+TV_SPLIT_Q4_0_WS = 3
 
 
 class TvError(RuntimeError):

@@ -729,9 +729,18 @@ static split_fn pick_split(int D, int kv, int nown, int nsh, bool mask)
     return nullptr;
 }
 
+// The warp-specialised kernel takes unmasked Q4_0 plans whose tile layout it
+// has (head_dim 256; one or two own tiles per wave, at most two shared).
+static split_fn pick_ws(const tv_attn_desc *d, const SplitPlan &p)
+{
+    if (d->kv_type != TV_KV_Q4_0 || p.mask) return nullptr;
+    return pick_split_q4ws(d->head_dim, p.rows.nown, p.rows.nsh);
+}
+
 int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p)
 {
     if (p.S == 0) return TV_SPLIT_NONE;
+    if (pick_ws(d, p)) return TV_SPLIT_Q4_0_WS;
     return d->kv_type == TV_KV_Q4_0 ? TV_SPLIT_Q4_0 : TV_SPLIT_F16;
 }
 
@@ -779,11 +788,13 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
                 a.has_skip |= skip > 0;
             }
         }
-        split_fn fn = pick_split(D, d->kv_type, plan.rows.nown, plan.rows.nsh, plan.mask != 0);
+        split_fn fn = pick_ws(d, plan);
+        const int threads = fn ? 512 : 256;
+        if (!fn) fn = pick_split(D, d->kv_type, plan.rows.nown, plan.rows.nsh, plan.mask != 0);
         if (!fn) return TV_E_SHAPE;
         dim3 grid(plan.S, Hkv, plan.rows.groups);
         void *args[] = {(void *)&a};
-        if (hipLaunchKernel((const void *)fn, grid, dim3(256), args, 0, stream) != hipSuccess) return TV_E_HIP;
+        if (hipLaunchKernel((const void *)fn, grid, dim3(threads), args, 0, stream) != hipSuccess) return TV_E_HIP;
     }
 
     MergeArgs mg;

@@ -165,11 +165,14 @@ __device__ __forceinline__ int vpos(int kappa)
     return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
 }
 
-template <int D, int KVT, bool WIDE_V = false>
+template <int D, int KVT, bool WIDE_V = false, bool WIDE_K = false>
 struct Stage {
     static constexpr int NB = D / 32;   // 32-wide blocks per row
     static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
-    static constexpr int KSTR = D + 8;  // K row stride in LDS (halves)
+    // K row stride in LDS (halves): D + 8, or with WIDE_K D + 16 (an odd
+    // multiple of 32 bytes, at which an S^T fragment read of 16 rows x 4
+    // lane groups of 16 bytes meets no bank conflict)
+    static constexpr int KSTR = WIDE_K ? D + 16 : D + 8;
     // V^T row stride in LDS (halves): 144 bytes, or with WIDE_V 160 bytes,
     // an odd multiple of 32, at which a PV fragment read (16 rows x 4 lane
     // groups of 16 bytes) meets no bank conflict. The Q4_0 kernels with
@@ -290,14 +293,14 @@ struct RowWalk {
 // the next group's rows or those zeros), and a padding row's partial state
 // is never written. `lds` must be free when store() starts; it is free
 // again on return (after a barrier).
-template <int D, int KVT, int NOWN, int NSH>
+template <int D, int KVT, int NOWN, int NSH, int NTH = 256>
 struct QStage {
     static constexpr int NS = NOWN + NSH;
     static constexpr int NB = D / 32;
     static constexpr int QSTR = D + 16;  // row stride (halves): 16 rows x 4 lanes of 2 dwords, 2-way at most
     static constexpr int NT = 4 * NOWN + NSH;  // tiles of a workgroup
     static constexpr int PR = D / 8;           // 16-byte pieces per row
-    static constexpr int RS = 256 / PR;        // rows between a thread's pieces
+    static constexpr int RS = NTH / PR;        // rows between a thread's pieces (NTH threads)
     static constexpr int NQ = (16 * NT + RS - 1) / RS;  // pieces per thread
     static_assert(NQ * RS * QSTR <= 2 * Stage<D, KVT>::ELEMS, "staged query rows fit both stages");
     u4v pc[NQ];
@@ -314,8 +317,8 @@ struct QStage {
         }
     }
 
-    __device__ __forceinline__ void store(int t0, const int (&tile)[NS], int tid, int col, int grp, _Float16 *lds,
-                                          h8 (&qf)[NS][NB]) const
+    // the rows into LDS (no barrier)
+    __device__ __forceinline__ void write_rows(int tid, _Float16 *lds) const
     {
         if constexpr (KVT == TV_KV_Q4_0) {
             // Rows go to LDS already in the fragments' element order, so that
@@ -341,6 +344,19 @@ struct QStage {
 #pragma unroll
             for (int j = 0; j < NQ; ++j) *(u4v *)(dst + j * RS * QSTR) = pc[j];
         }
+    }
+
+    // fragment of block bb for lane (col, grp) of the tile whose first row is
+    // row tl0 of the group
+    static __device__ __forceinline__ h8 frag(const _Float16 *lds, int tl0, int col, int grp, int bb)
+    {
+        return *(const h8 *)(lds + (tl0 + col) * QSTR + 8 * grp + 32 * bb);
+    }
+
+    __device__ __forceinline__ void store(int t0, const int (&tile)[NS], int tid, int col, int grp, _Float16 *lds,
+                                          h8 (&qf)[NS][NB]) const
+    {
+        write_rows(tid, lds);
         __syncthreads();
         // every LDS read is issued before the first is used (left to itself
         // the compiler keeps one or two in flight and each waits out the
@@ -455,5 +471,8 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
 }
 
 split_fn pick_split_q4(int D, int nown, int nsh, bool mask);
+// The warp-specialised Q4_0 kernel (512 threads) for a tile layout, or null
+// when it has none (head_dim other than 256, other layouts).
+split_fn pick_split_q4ws(int D, int nown, int nsh);
 
 }  // namespace tv
