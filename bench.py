@@ -152,7 +152,7 @@ def main():
     lg = torch.from_numpy(logits).to(dev)
     am = torch.empty(n, dtype=torch.int32, device=dev)
     res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
-    aws = torch.empty(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
+    aws = torch.zeros(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     # chain-16 comparison (same cache, block-size-16 chain instead of the tree)
@@ -291,7 +291,7 @@ def full_step(tv, synth, dev, stream, steps):
     lg = torch.from_numpy(logits).to(dev)
     am = torch.empty(n, dtype=torch.int32, device=dev)
     res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
-    aws = torch.empty(tv.tv_accept_workspace_bytes(n, w["vocab"]), dtype=torch.uint8, device=dev)
+    aws = torch.zeros(tv.tv_accept_workspace_bytes(n, w["vocab"]), dtype=torch.uint8, device=dev)
     host = torch.empty(2 + 2 * n, dtype=torch.int32, pin_memory=True)
     # every layer's cache has the same shape and strides: one commit launch
     k_trees, v_trees = [t["k_tree"] for t in layers], [t["v_tree"] for t in layers]

@@ -192,7 +192,11 @@ TV_API int tv_attn_plan(const tv_attn_desc *d, int32_t n_cu, tv_attn_plan_info *
 TV_API int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
                      void *stream);
 
-/* Device workspace (bytes) tree_accept needs for n_nodes x vocab logits. */
+/*
+ * Device workspace (bytes) tree_accept needs for n_nodes x vocab logits:
+ * completion counters and one running maximum per node, 832 bytes for any
+ * valid shape. 0 for n_nodes outside 1..TV_MAX_NODES or vocab < 1.
+ */
 TV_API size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab);
 
 /*
@@ -216,7 +220,14 @@ TV_API size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab);
  *             child's token equals its parent's argmax; among equally long
  *             ones, the one with the smaller child index where they diverge.
  * workspace   device, tv_accept_workspace_bytes(n_nodes, vocab) bytes,
- *             8-byte aligned, overwritten.
+ *             8-byte aligned, all zero before the first call that uses it
+ *             (e.g. zeroed once when allocated); every call leaves it zero
+ *             again, so a workspace can be reused call after call on one
+ *             stream. Calls that share a workspace must not overlap (one
+ *             stream, or ordered streams).
+ * One launch: every workgroup reduces one 8192-logit slice of one row into
+ * the row's maximum with device-scope atomics; the workgroup that completes
+ * the last row runs the walk.
  */
 TV_API int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
                 const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *workspace,

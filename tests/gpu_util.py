@@ -53,7 +53,7 @@ def gpu_accept(logits, parent, tokens, dev="cuda"):
     lg = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to(dev)
     am = torch.full((n,), -7, dtype=torch.int32, device=dev)
     res = torch.full((2 + 2 * n,), -7, dtype=torch.int32, device=dev)
-    ws = torch.empty(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
     tv.tree_accept(lg, parent, tokens, am, res, ws)
     torch.cuda.synchronize()
     return am.cpu().numpy(), res.cpu().numpy()

@@ -87,3 +87,28 @@ def test_64_node_tree():
     tok = synth.sibling_distinct_tokens(rng, parent, 1000)
     logits, L, _ = synth.planted_logits(rng, parent, tok, 1000)
     assert check(logits, parent, tok)[0] == L
+
+
+def test_workspace_reused_across_calls():
+    """One workspace for many calls of different sizes on one stream: the
+    counters and maxima the last workgroup resets must be zero again for the
+    next call (results bit-exact each time, workspace zero at the end)."""
+    import torch
+
+    import tree_verify_attention_ddtree_amd as tv
+    V = synth.WORKLOADS["full"]["vocab"]
+    ws = torch.zeros(tv.tv_accept_workspace_bytes(64, V), dtype=torch.uint8, device="cuda")
+    for t, (n, vocab) in enumerate([(23, V), (8, 1024), (64, 5000), (23, V), (1, 7), (40, 70001)]):
+        s = synth.streams(7100 + t)
+        parent = synth.draft_tree(s["tree"], n, 16)
+        tok = synth.sibling_distinct_tokens(s["tokens"], parent, vocab)
+        logits, L, _ = synth.planted_logits(s["logits"], parent, tok, vocab)
+        lg = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+        am = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        res = torch.full((2 + 2 * n,), -7, dtype=torch.int32, device="cuda")
+        tv.tree_accept(lg, parent, tok, am, res, ws)
+        torch.cuda.synchronize()
+        ram, rres = oracle.accept(logits, parent, tok)
+        assert np.array_equal(am.cpu().numpy(), ram) and np.array_equal(res.cpu().numpy(), rres), (n, vocab)
+        assert int(rres[0]) == L
+    assert int(ws.sum().item()) == 0

@@ -143,7 +143,7 @@ def test_accept_then_commit_on_device():
     lg = torch.from_numpy(logits).to(dev)
     am = torch.empty(n, dtype=torch.int32, device=dev)
     res = torch.empty(2 + 2 * n, dtype=torch.int32, device=dev)
-    ws = torch.empty(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tv.tv_accept_workspace_bytes(n, vocab), dtype=torch.uint8, device=dev)
     tk, tvv = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
     ts, hs = tv.cache_strides(tk, tv.TV_KV_Q4_0)
     tv.tree_accept(lg, parent, tokens, am, res, ws)
@@ -221,7 +221,7 @@ def test_decode_loop_matches_oracle(kv):
         tv.tree_verify_attn(desc, gk, gv, qd, ktd, vtd, out, ws, wsb)
         am = torch.empty(N, dtype=torch.int32, device=dev)
         res = torch.empty(2 + 2 * N, dtype=torch.int32, device=dev)
-        aws = torch.empty(tv.tv_accept_workspace_bytes(N, VOCAB), dtype=torch.uint8, device=dev)
+        aws = torch.zeros(tv.tv_accept_workspace_bytes(N, VOCAB), dtype=torch.uint8, device=dev)
         tv.tree_accept(torch.from_numpy(lg).to(dev), parent, tokens, am, res, aws)
         tv.tree_commit_kv(tv.make_commit_desc(N, HKV, D, kvt, n_ctx, CAP, ts, hs), res, ktd, vtd, gk, gv)
         torch.cuda.synchronize()

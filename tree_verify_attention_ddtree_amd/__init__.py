@@ -208,7 +208,10 @@ def tv_accept_workspace_bytes(n_nodes: int, vocab: int) -> int:
 def tree_accept(logits, parent, tokens, argmax_out, result_out, workspace, stream=None) -> None:
     """Greedy acceptance (see include/tree_verify.h). ``logits`` is a device
     fp32 [n, vocab] tensor, ``parent``/``tokens`` host int sequences,
-    ``argmax_out`` device int32 [n], ``result_out`` device int32 [2 + 2n]."""
+    ``argmax_out`` device int32 [n], ``result_out`` device int32 [2 + 2n].
+    ``workspace`` holds tv_accept_workspace_bytes(n, vocab) bytes, zero
+    before its first use (allocate it with torch.zeros); every call leaves it
+    zero."""
     n, vocab = int(logits.shape[0]), int(logits.shape[1])
     par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
     tok = np.ascontiguousarray(np.asarray(tokens), dtype=np.int32)

@@ -1,5 +1,5 @@
 // Greedy acceptance for gfx950: per-node argmax over the vocabulary, then the
-// walk down the draft tree.
+// walk down the draft tree, in one launch.
 //
 // Method: verification is greedy; the engine accepts the draft tokens along
 // the tree while they equal the target's argmax, and the target's argmax at
@@ -7,14 +7,15 @@
 // 2倍のスループットを目指すQwen3.6-27B", feature list and constraints: greedy
 // verify only, sampling parameters ignored).
 //
-// Kernel 1 (argmax_partial): grid (chunks, n). Each workgroup scans one slice
-// of one logits row with 16-byte loads and reduces a 64-bit key
-// (order-preserving float code << 32 | ~index) so that the maximum key is the
-// largest value with the smallest index; NaN maps to the lowest code and -0 to
-// the code of +0.
-// Kernel 2 (finish_walk): one wave, lane i = node i: reduces the slices of
-// row i, then finds the accepted path from ballots over the nodes' ancestor
-// masks (built on the host from the parent array).
+// accept_kernel, grid (slices, n): each workgroup scans one slice of one
+// logits row with 16-byte loads and reduces a 64-bit key (order-preserving
+// float code << 32 | ~index), so that the maximum key is the largest value
+// with the smallest index (NaN maps to the lowest code, -0 to the code of
+// +0), and stores it. A completion counter then picks the workgroup that
+// finishes last; its first wave (lane i = node i) reduces every row's slice
+// keys and finds the accepted path from ballots over the nodes' ancestor
+// masks (built on the host from the parent array), and sets the counter back
+// to zero for the next call.
 
 #include "tv_internal.h"
 
@@ -49,53 +50,22 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t v)
     return v;
 }
 
-__global__ void __launch_bounds__(kAccThreads) argmax_partial(const float *logits, int vocab, int n_slices,
-                                                              uint64_t *part)
-{
-    constexpr int PER = kSliceFloats / (4 * kAccThreads);  // 16-byte loads per thread
-    const int row = blockIdx.y, sl = blockIdx.x;
-    const int64_t lo = (int64_t)sl * kSliceFloats;
-    const int64_t hi = lo + kSliceFloats < vocab ? lo + kSliceFloats : vocab;
-    const float *r = logits + (int64_t)row * vocab;
-    uint64_t best = 0;  // below every key
-    // 16-byte loads where the row allows them (rows start 16-byte aligned
-    // only when vocab is a multiple of 4); all of a thread's loads are issued
-    // before the first compare.
-    if ((vocab & 3) == 0) {
-        float4 x[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
-            x[k] = v < hi ? *(const float4 *)(r + v) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
-            if (v < hi) {
-                best = umax64(best, pack_key(x[k].x, (uint32_t)v));
-                best = umax64(best, pack_key(x[k].y, (uint32_t)v + 1));
-                best = umax64(best, pack_key(x[k].z, (uint32_t)v + 2));
-                best = umax64(best, pack_key(x[k].w, (uint32_t)v + 3));
-            }
-        }
-    } else {
-        for (int64_t v = lo + threadIdx.x; v < hi; v += kAccThreads) best = umax64(best, pack_key(r[v], (uint32_t)v));
-    }
-    best = wave_umax64(best);
-    __shared__ uint64_t red[kAccThreads / 64];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t b = red[0];
-        for (int w = 1; w < kAccThreads / 64; ++w) b = umax64(b, red[w]);
-        part[(int64_t)row * n_slices + sl] = b;
-    }
-}
+// Workspace (all of it zero before the first call; the last workgroup of
+// every call sets it back to zero): the count of rows done, then one slice
+// counter and one running maximum key per row.
+constexpr size_t kRowsDoneOff = 0;
+constexpr size_t kRowCountOff = 64;
+constexpr size_t kRowKeyOff = kRowCountOff + 4 * TV_MAX_NODES;
+constexpr size_t kAcceptWsBytes = kRowKeyOff + 8 * TV_MAX_NODES;
 
-struct WalkArgs {
-    const uint64_t *part;
+struct AcceptArgs {
+    const float *logits;
+    uint32_t *rows_done;
+    uint32_t *row_count;  // [n] slices done per row
+    uint64_t *row_key;    // [n] maximum key per row
     int32_t *argmax_out;
     int32_t *result_out;
+    int32_t vocab;
     int32_t n;
     int32_t n_slices;
     int32_t parent[TV_MAX_NODES];
@@ -103,34 +73,22 @@ struct WalkArgs {
     uint64_t anc[TV_MAX_NODES];  // ancestor-or-self mask of each node
 };
 
-// One wave; lane i stands for tree node i (its parent, token and
+// The walk, by one wave; lane i stands for tree node i (its parent, token and
 // ancestor-or-self mask come from the kernel arguments).
-//   1. a[i]: lane i reduces the slice maxima of row i.
+//   1. a[i]: lane i reads the maximum key of row i.
 //   2. Node i matches when its token equals its parent's argmax; it is on an
 //      accepted path when every node of its root path matches, i.e. its
 //      ancestor mask lies inside the ballot of matching nodes.
 //   3. The deepest such nodes mark their root paths; the descent from the
 //      root takes, at every level, the smallest child on a marked path, which
 //      is the lexicographically smallest of the longest accepted paths.
-// Only the parent's argmax crosses lanes through LDS; the rest are ballots
-// and lane reads of uniform indices.
-__global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
+// Only the parent's argmax crosses lanes; the rest are ballots and lane reads
+// of uniform indices.
+__device__ void walk(const AcceptArgs &a, int lane)
 {
-    const int lane = threadIdx.x;
     const int n = a.n;
     const bool live = lane < n;
-    // the slice maxima of row `lane` (a dead lane reads row 0), loaded 32 at a
-    // time with no branch around a load, so that the first 32 are in flight
-    // together with the per-lane argument reads below
-    const uint64_t *pr = a.part + (int64_t)(live ? lane : 0) * a.n_slices;
-    uint64_t b = 0;
-    for (int s0 = 0; s0 < a.n_slices; s0 += 32) {
-        uint64_t v[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) v[k] = pr[s0 + k < a.n_slices ? s0 + k : 0];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) b = umax64(b, v[k]);
-    }
+    const uint64_t b = __hip_atomic_load(a.row_key + (live ? lane : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int par = live ? a.parent[lane] : -1;
     const int tok = live ? a.tokens[lane] : -1;
     const uint64_t anc = live ? a.anc[lane] : 0ull;
@@ -198,39 +156,114 @@ __global__ void __launch_bounds__(64) finish_walk(const WalkArgs a)
     }
 }
 
+__global__ void __launch_bounds__(kAccThreads) accept_kernel(const AcceptArgs a)
+{
+    constexpr int PER = kSliceFloats / (4 * kAccThreads);  // 16-byte loads per thread
+    const int row = blockIdx.y, sl = blockIdx.x;
+    const int vocab = a.vocab;
+    const int64_t lo = (int64_t)sl * kSliceFloats;
+    const int64_t hi = lo + kSliceFloats < vocab ? lo + kSliceFloats : vocab;
+    const float *r = a.logits + (int64_t)row * vocab;
+    uint64_t best = 0;  // below every key
+    // 16-byte loads where the row allows them (rows start 16-byte aligned
+    // only when vocab is a multiple of 4); all of a thread's loads are issued
+    // before the first compare.
+    if ((vocab & 3) == 0) {
+        float4 x[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
+            x[k] = v < hi ? *(const float4 *)(r + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t v = lo + 4 * threadIdx.x + 4 * kAccThreads * k;
+            if (v < hi) {
+                best = umax64(best, pack_key(x[k].x, (uint32_t)v));
+                best = umax64(best, pack_key(x[k].y, (uint32_t)v + 1));
+                best = umax64(best, pack_key(x[k].z, (uint32_t)v + 2));
+                best = umax64(best, pack_key(x[k].w, (uint32_t)v + 3));
+            }
+        }
+    } else {
+        for (int64_t v = lo + threadIdx.x; v < hi; v += kAccThreads) best = umax64(best, pack_key(r[v], (uint32_t)v));
+    }
+    best = wave_umax64(best);
+    __shared__ uint64_t red[kAccThreads / 64];
+    __shared__ int last;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t b = red[0];
+        for (int w = 1; w < kAccThreads / 64; ++w) b = umax64(b, red[w]);
+        // Device-scope atomics only, each finished (returned) before the
+        // next is issued: the slice key into the row's maximum, then the
+        // row's slice count; the row's last slice counts the row done, and
+        // the workgroup that counts the last row runs the walk. Every
+        // maximum is in place before its row counts as done, and every row
+        // before the last count, so the walk reads final keys.
+        const uint64_t prev =
+            __hip_atomic_fetch_max(a.row_key + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // (no key has all 64 bits set: NaN maps to code 0; the test only
+        // makes the count wait for the maximum's return)
+        const uint32_t inc = prev == ~0ull ? 2u : 1u;
+        const uint32_t d = __hip_atomic_fetch_add(a.row_count + row, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int is_last = 0;
+        if (d == (uint32_t)a.n_slices - 1) {
+            const uint32_t r = __hip_atomic_fetch_add(a.rows_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = r == (uint32_t)a.n - 1;
+        }
+        last = is_last;
+    }
+    __syncthreads();
+    if (!last) return;
+    if (threadIdx.x < 64) {
+        walk(a, threadIdx.x);
+        // leave the workspace zero for the next call
+        if (threadIdx.x < a.n) {
+            __hip_atomic_store(a.row_key + threadIdx.x, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.row_count + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(a.rows_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 static int64_t n_slices_for(int vocab) { return ((int64_t)vocab + kSliceFloats - 1) / kSliceFloats; }
 
-size_t accept_ws_bytes(int n, int vocab) { return (size_t)n * (size_t)n_slices_for(vocab) * sizeof(uint64_t); }
+size_t accept_ws_bytes(int, int) { return kAcceptWsBytes; }
+
+static int launch_accept_on(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
+                            int32_t *argmax_out, int32_t *result_out, uint8_t *ws, hipStream_t stream)
+{
+    AcceptArgs a;
+    a.logits = logits;
+    a.rows_done = (uint32_t *)(ws + kRowsDoneOff);
+    a.row_count = (uint32_t *)(ws + kRowCountOff);
+    a.row_key = (uint64_t *)(ws + kRowKeyOff);
+    a.argmax_out = argmax_out;
+    a.result_out = result_out;
+    a.vocab = vocab;
+    a.n = n;
+    a.n_slices = (int)n_slices_for(vocab);
+    for (int i = 0; i < TV_MAX_NODES; ++i) {
+        a.parent[i] = i < n ? parent[i] : -1;
+        a.tokens[i] = i < n ? tokens[i] : -1;
+        uint64_t m = 0;
+        if (i < n)
+            for (int v = i; v >= 0; v = parent[v]) m |= 1ull << v;
+        a.anc[i] = m;
+    }
+    void *args[] = {(void *)&a};
+    if (hipLaunchKernel((const void *)accept_kernel, dim3(a.n_slices, n), dim3(kAccThreads), args, 0, stream) !=
+        hipSuccess)
+        return TV_E_HIP;
+    return TV_OK;
+}
 
 int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream)
 {
-    const int ns = (int)n_slices_for(vocab);
-    uint64_t *part = (uint64_t *)ws;
-    {
-        void *args[] = {(void *)&logits, (void *)&vocab, (void *)&ns, (void *)&part};
-        if (hipLaunchKernel((const void *)argmax_partial, dim3(ns, n), dim3(kAccThreads), args, 0, stream) !=
-            hipSuccess)
-            return TV_E_HIP;
-    }
-    WalkArgs w;
-    w.part = part;
-    w.argmax_out = argmax_out;
-    w.result_out = result_out;
-    w.n = n;
-    w.n_slices = ns;
-    for (int i = 0; i < TV_MAX_NODES; ++i) {
-        w.parent[i] = i < n ? parent[i] : -1;
-        w.tokens[i] = i < n ? tokens[i] : -1;
-        uint64_t m = 0;
-        if (i < n)
-            for (int v = i; v >= 0; v = parent[v]) m |= 1ull << v;
-        w.anc[i] = m;
-    }
-    void *wargs[] = {(void *)&w};
-    if (hipLaunchKernel((const void *)finish_walk, dim3(1), dim3(64), wargs, 0, stream) != hipSuccess)
-        return TV_E_HIP;
-    return TV_OK;
+    return launch_accept_on(logits, n, vocab, parent, tokens, argmax_out, result_out, (uint8_t *)ws, stream);
 }
 
 }  // namespace tv

@@ -285,14 +285,22 @@ size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab)
     return tv::accept_ws_bytes(n_nodes, vocab);
 }
 
-int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent, const int32_t *tokens,
-                int32_t *argmax_out, int32_t *result_out, void *workspace, size_t workspace_bytes, void *stream)
+static int check_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
+                        const int32_t *tokens, const int32_t *argmax_out, const int32_t *result_out)
 {
     int rc = tv::check_tree(n_nodes, parent);
     if (rc) return rc;
     if (vocab < 1) return TV_E_SHAPE;
     if (!logits || !tokens || !argmax_out || !result_out) return TV_E_ARG;
     if (!aligned(logits, 16) || !aligned(argmax_out, 4) || !aligned(result_out, 4)) return TV_E_ALIGN;
+    return TV_OK;
+}
+
+int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent, const int32_t *tokens,
+                int32_t *argmax_out, int32_t *result_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = check_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out);
+    if (rc) return rc;
     const size_t need = tv::accept_ws_bytes(n_nodes, vocab);
     if (!workspace || workspace_bytes < need) return TV_E_WORKSPACE;
     if (!aligned(workspace, 8)) return TV_E_ALIGN;
