@@ -234,6 +234,21 @@ TV_API int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, cons
                 size_t workspace_bytes, void *stream);
 
 /*
+ * tree_accept without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, checks and results as tree_accept
+ * (n_nodes up to TV_MAX_NODES, any vocab >= 1; anything larger is
+ * TV_E_SHAPE). The acceptance state (832 bytes of counters and row maxima)
+ * lives in a static array of the library, one per device, held until the
+ * process ends: zero when the library loads, and every call leaves it zero.
+ * All calls on one device share that array, so calls that overlap on one
+ * device race: serialise them (one stream, or ordered streams). Nothing is
+ * allocated; the first call on a device looks up the array's address there.
+ */
+TV_API int tree_accept_noalloc(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
+                               const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *stream);
+
+/*
  * Shape of one layer's KV commit.
  *
  * n_nodes      size of the verified tree, 1..TV_MAX_NODES.

@@ -106,6 +106,8 @@ def lib():
         L.tree_commit_kv.restype = ctypes.c_int
         L.tree_commit_kv_layers.argtypes = [ctypes.POINTER(TvCommitDesc), ctypes.c_int32, P, P, P, P, P, P]
         L.tree_commit_kv_layers.restype = ctypes.c_int
+        L.tree_accept_noalloc.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+        L.tree_accept_noalloc.restype = ctypes.c_int
         L.tv_attn_plan.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.POINTER(TvAttnPlanInfo)]
         L.tv_attn_plan.restype = ctypes.c_int
         _lib = L
@@ -126,7 +128,7 @@ class TvCommitDesc(ctypes.Structure):
 
 
 EXPORTS = ("tree_verify_attn", "tree_accept", "tree_commit_kv", "tree_commit_kv_layers", "tv_attn_workspace_bytes",
-           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan")
+           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan", "tree_accept_noalloc")
 
 
 def tv_strerror(code: int) -> str:
@@ -223,6 +225,22 @@ def tree_accept(logits, parent, tokens, argmax_out, result_out, workspace, strea
                            _ptr(workspace), int(wsb), _stream_ptr(stream))
     if rc != TV_OK:
         raise TvError(rc, "tree_accept")
+
+
+def tree_accept_noalloc(logits, parent, tokens, argmax_out, result_out, stream=None) -> None:
+    """tree_accept without a workspace (the library's per-device static
+    state; see include/tree_verify.h): for callers that cannot allocate.
+    Calls on one device must not overlap."""
+    n, vocab = int(logits.shape[0]), int(logits.shape[1])
+    par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
+    tok = np.ascontiguousarray(np.asarray(tokens), dtype=np.int32)
+    if len(par) != n or len(tok) != n:
+        raise ValueError("parent/tokens length must equal logits.shape[0]")
+    rc = lib().tree_accept_noalloc(_ptr(logits), n, vocab, par.ctypes.data_as(ctypes.c_void_p),
+                                   tok.ctypes.data_as(ctypes.c_void_p), _ptr(argmax_out), _ptr(result_out),
+                                   _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_accept_noalloc")
 
 
 def make_commit_desc(n_nodes, n_kv_heads, head_dim, kv_type, n_ctx, capacity, kv_token_stride, kv_head_stride):

@@ -17,6 +17,8 @@
 // masks (built on the host from the parent array), and sets the counter back
 // to zero for the next call.
 
+#include <mutex>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -264,6 +266,38 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream)
 {
     return launch_accept_on(logits, n, vocab, parent, tokens, argmax_out, result_out, (uint8_t *)ws, stream);
+}
+
+// State of tree_accept_noalloc: the acceptance workspace as a static device
+// array, one per device (zero when the module loads; every call leaves it
+// zero). Host code never passes the array's name to a kernel: the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+static __device__ __align__(256) uint64_t scratch[kAcceptWsBytes / sizeof(uint64_t)];
+
+static int scratch_ptr(uint8_t **out)
+{
+    static std::mutex mu;
+    static void *ptrs[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return TV_E_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TV_E_HIP;
+        ptrs[dev] = p;
+    }
+    *out = (uint8_t *)ptrs[dev];
+    return TV_OK;
+}
+
+int launch_accept_noalloc(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
+                          int32_t *argmax_out, int32_t *result_out, hipStream_t stream)
+{
+    uint8_t *ws = nullptr;
+    const int rc = scratch_ptr(&ws);
+    if (rc) return rc;
+    return launch_accept_on(logits, n, vocab, parent, tokens, argmax_out, result_out, ws, stream);
 }
 
 }  // namespace tv

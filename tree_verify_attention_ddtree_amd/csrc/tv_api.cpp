@@ -16,6 +16,8 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
 size_t accept_ws_bytes(int n, int vocab);
 int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
+int launch_accept_noalloc(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
+                          int32_t *argmax_out, int32_t *result_out, hipStream_t stream);
 int launch_commit(const tv_commit_desc *d, int n_layers, const int32_t *result, const void *const *k_tree,
                   const void *const *v_tree, void *const *k_cache, void *const *v_cache, hipStream_t stream);
 
@@ -306,6 +308,15 @@ int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32
     if (!aligned(workspace, 8)) return TV_E_ALIGN;
     return tv::launch_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out, workspace,
                              (hipStream_t)stream);
+}
+
+int tree_accept_noalloc(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
+                        const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *stream)
+{
+    int rc = check_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out);
+    if (rc) return rc;
+    return tv::launch_accept_noalloc(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out,
+                                     (hipStream_t)stream);
 }
 
 static int check_commit_desc(const tv_commit_desc *d)
