@@ -20,4 +20,8 @@ from .workloads import (  # noqa: F401
     sibling_distinct_tokens,
     planted_logits,
     attn_inputs,
+    full_step_tree,
+    full_step_cache,
+    full_step_qkv,
+    full_step_layer,
 )

@@ -190,3 +190,48 @@ def attn_inputs(n_q_heads: int, n_kv_heads: int, head_dim: int, n_ctx: int, n_no
         k_tree=f16_normal(s["k_tree"], (n, n_kv_heads, head_dim)),
         v_tree=f16_normal(s["v_tree"], (n, n_kv_heads, head_dim)),
     )
+
+
+def full_step_tree(tree: int) -> dict:
+    """Tree `tree` (0..63) of the 16-layer verify step: the draft tree shared
+    by every layer of that step, its sibling-distinct draft tokens and the
+    planted logits of the acceptance (seed 5000 + tree)."""
+    w = WORKLOADS["full"]
+    s = streams(5000 + tree)
+    parent = draft_tree(s["tree"], w["n_nodes"], w["depth_cap"])
+    tokens = sibling_distinct_tokens(s["tokens"], parent, w["vocab"])
+    logits, L, path = planted_logits(s["logits"], parent, tokens, w["vocab"])
+    return dict(parent=parent, tokens=tokens, logits=logits, n_acc=L, path=path)
+
+
+def full_step_cache(layer: int):
+    """Layer `layer`'s committed Q4_0 caches (K, V) of the verify step
+    (the cache streams of seed 5000 + 100 * layer)."""
+    w = WORKLOADS["full"]
+    s = streams(5000 + 100 * layer)
+    kc = q4_0_cache(s["k_cache"], w["n_kv_heads"], w["n_ctx"], w["head_dim"])
+    vc = q4_0_cache(s["v_cache"], w["n_kv_heads"], w["n_ctx"], w["head_dim"])
+    return kc, vc
+
+
+def full_step_qkv(layer: int, tree: int, n: int) -> dict:
+    """Q, K_tree and V_tree of layer `layer` for tree `tree` (seed
+    1000000 + 100 * layer + tree): fp16 N(0,1)."""
+    w = WORKLOADS["full"]
+    s = streams(1000000 + 100 * layer + tree)
+    return dict(q=f16_normal(s["q"], (n, w["n_q_heads"], w["head_dim"])),
+                k_tree=f16_normal(s["k_tree"], (n, w["n_kv_heads"], w["head_dim"])),
+                v_tree=f16_normal(s["v_tree"], (n, w["n_kv_heads"], w["head_dim"])))
+
+
+def full_step_layer(layer: int, tree: int, cache=None, tree_inputs=None) -> dict:
+    """One layer's attention inputs of the verify step for tree `tree`, in
+    the form attn_inputs returns (the caches may be passed in, since they do
+    not depend on the tree)."""
+    w = WORKLOADS["full"]
+    t = tree_inputs if tree_inputs is not None else full_step_tree(tree)
+    kc, vc = cache if cache is not None else full_step_cache(layer)
+    n = len(t["parent"])
+    return dict(kv="q4_0", n_q_heads=w["n_q_heads"], n_kv_heads=w["n_kv_heads"], head_dim=w["head_dim"],
+                n_ctx=w["n_ctx"], window=0, scale=1.0 / np.sqrt(w["head_dim"]), parent=t["parent"],
+                k_cache=kc, v_cache=vc, **full_step_qkv(layer, tree, n))

@@ -76,6 +76,29 @@ def test_long_128k_sampled(tree):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("tree", ["budget22", "chain16"])
+def test_long_128k_all_rows(tree):
+    """The headline layer (131072 Q4_0 rows, 24 q / 4 kv heads, head_dim
+    256) on every output row: 552 for the budget-22 tree, 384 for the
+    chain of 16."""
+    w = dict(synth.WORKLOADS["long"])
+    parent = synth.chain_tree(16) if tree == "chain16" else None
+    inp = synth.attn_inputs(**w, parent=parent)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("layer,tree", [(0, 0), (0, 1), (15, 0), (15, 1)])
+def test_full_step_layer_tree_all_rows(layer, tree):
+    """Layers 0 and 15 of the 16-layer verify step at 32768 rows, for trees 0
+    and 1 of its 64 (one draft tree per step, shared by every layer), on every
+    output row."""
+    t = synth.full_step_tree(tree)
+    inp = synth.full_step_layer(layer, tree, tree_inputs=t)
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, (layer, tree, err)
+
+
 def test_window_61k():
     w = dict(synth.WORKLOADS["window"])
     inp = synth.attn_inputs(**w)
@@ -318,6 +341,71 @@ def test_peaky_scores_force_rescaling_q4_0(n_nodes):
     inp["k_cache"] = c
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
+
+
+def _ramped_q4_0(alpha, n_ctx=20000, n_nodes=23, seed=2):
+    """The 27B layout with queries scaled by alpha and Q4_0 key scales that
+    rise 30-fold over every 256 rows, rounded to fp16 as they are (not to
+    powers of two): scores grow with alpha."""
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=n_ctx, n_nodes=n_nodes, seed=seed))
+    inp["q"] = (inp["q"].astype(np.float32) * alpha).astype(np.float16)
+    c = inp["k_cache"].copy()
+    blocks = c.reshape(c.shape[0], c.shape[1], -1, 18)
+    sc = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float32)
+    ramp = (0.2 + 5.8 * (np.arange(c.shape[1]) % 256) / 255.0).astype(np.float32)[None, :, None]
+    sc16 = (sc * ramp).astype(np.float16)
+    blocks[..., 0:2] = sc16[..., None].view(np.uint8).reshape(sc16.shape + (2,))
+    inp["k_cache"] = c
+    return inp
+
+
+def test_q4_0_precision_edge_ordinary_scales():
+    """The documented limit of the Q4_0 path: each dequantised key is rounded
+    to fp16 once, which moves a score by up to 2^-11 of its terms, so the row
+    error grows with the scores. With ordinary key scales (rising 30-fold
+    over every 256 rows) and queries x1.5 the largest |scale q.k| is about 23
+    in log2 units, inside the stated bound of 29, and the error stays within
+    2e-3 (measured 0.8e-3 at x1 and 2.0e-3 at x2, where the scores reach 31)."""
+    inp = _ramped_q4_0(1.5)
+    D, G = inp["head_dim"], inp["n_q_heads"] // inp["n_kv_heads"]
+    k = oracle.q4_0_dequant(inp["k_cache"], D)
+    q = inp["q"].astype(np.float64)
+    c = inp["scale"] * np.log2(np.e)
+    smax = max(float(np.abs((q[:, h, :] @ k[h // G].T) * c).max()) for h in range(inp["n_q_heads"]))
+    assert 20.0 < smax < 29.0, smax
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+def test_split_count_invariance(kv):
+    """The same attention under different split plans: the 24 q / 4 kv layer
+    at 32768 rows runs 64 key-range splits per KV head; each KV head called
+    alone (6 q / 1 kv heads, the same rows) runs 256. Both within 2e-3 of the
+    oracle and of each other."""
+    import tree_verify_attention_ddtree_amd as tv
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=32768, seed=61), kv=kv)
+    kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+    row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
+    whole = gpu_attn(inp).astype(np.float64)
+    d4, _p4 = tv.make_desc(inp["parent"], 24, 4, 256, kvt, 32768, 0, inp["scale"], row, row * 32768)
+    d1, _p1 = tv.make_desc(inp["parent"], 6, 1, 256, kvt, 32768, 0, inp["scale"], row, row * 32768)
+    s4, s1 = tv.tv_attn_plan(d4)["splits"], tv.tv_attn_plan(d1)["splits"]
+    assert s1 >= 2 * s4, (s4, s1)
+    parts = []
+    for g in range(4):
+        sub = dict(inp, n_q_heads=6, n_kv_heads=1, q=np.ascontiguousarray(inp["q"][:, 6 * g:6 * g + 6]),
+                   k_tree=np.ascontiguousarray(inp["k_tree"][:, g:g + 1]),
+                   v_tree=np.ascontiguousarray(inp["v_tree"][:, g:g + 1]),
+                   k_cache=np.ascontiguousarray(inp["k_cache"][g:g + 1]),
+                   v_cache=np.ascontiguousarray(inp["v_cache"][g:g + 1]))
+        parts.append(gpu_attn(sub).astype(np.float64))
+    split = np.concatenate(parts, axis=1)
+    rows = sample_rows(23, 24, 48, 61)
+    ref = oracle.attn(inp, rows=rows)
+    assert check_rows(whole, ref, rows, 24) <= TOL
+    assert check_rows(split, ref, rows, 24) <= TOL
+    assert rownorm_err(split, whole) <= TOL
 
 
 def test_deterministic():
