@@ -326,6 +326,25 @@ TV_API int tree_commit_kv_layers(const tv_commit_desc *d, int32_t n_layers, cons
                           const void *const *k_tree, const void *const *v_tree, void *const *k_cache,
                           void *const *v_cache, void *stream);
 
+/* Kinds of tv_stream_probe. */
+#define TV_PROBE_READ 0        /* read every byte */
+#define TV_PROBE_Q4_0_DECODE 1 /* read, and unpack every byte as Q4_0 codes times a scale */
+
+/*
+ * Diagnostic: streams `bytes` bytes of device memory from `buf` (16-byte
+ * aligned, a multiple of 16 bytes) with no attention arithmetic, to measure
+ * the rate a streaming kernel reaches on this GPU next to the attention
+ * kernels' own. TV_PROBE_READ only reads; TV_PROBE_Q4_0_DECODE also turns
+ * every 4-bit code into fp16 (code - 8) * scale, with the instruction mix
+ * the split kernels use (the scale is a constant; block scales are not
+ * parsed). n_checksums workgroups (1 .. 2^20) each write one checksum word to
+ * the device array `checksums` (4-byte aligned), whose values only keep the
+ * reads from being optimised away. Asynchronous on `stream`.
+ * Returns TV_OK or a TV_E_* code (nothing is launched on error).
+ */
+TV_API int tv_stream_probe(const void *buf, uint64_t bytes, int32_t kind, uint32_t *checksums,
+                           int32_t n_checksums, void *stream);
+
 /* Static string for a status code. */
 TV_API const char *tv_strerror(int code);
 

@@ -74,6 +74,18 @@ def lib():
     return _lib
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads the oracle uses from now on (the GNU OpenMP runtime the
+    library is linked against)."""
+    lib()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    lib()
+    return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+
+
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 

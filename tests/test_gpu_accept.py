@@ -112,3 +112,22 @@ def test_workspace_reused_across_calls():
         assert np.array_equal(am.cpu().numpy(), ram) and np.array_equal(res.cpu().numpy(), rres), (n, vocab)
         assert int(rres[0]) == L
     assert int(ws.sum().item()) == 0
+
+
+def test_stream_probe_reads_every_byte():
+    """tv_stream_probe: the checksums of all workgroups XOR to the XOR of
+    every dword of the buffer (each 16-byte piece is read by exactly one
+    thread); the decoding kind runs on the same buffer."""
+    import torch
+
+    import tree_verify_attention_ddtree_amd as tv
+    rng = np.random.default_rng(5)
+    buf_np = rng.integers(0, 2 ** 32, size=(1 << 20) + 12, dtype=np.uint32)
+    buf = torch.from_numpy(buf_np.view(np.int32)).cuda()
+    chk = torch.zeros(96, dtype=torch.int32, device="cuda")
+    tv.tv_stream_probe(buf, tv.TV_PROBE_READ, chk)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(chk.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(buf_np))
+    tv.tv_stream_probe(buf, tv.TV_PROBE_Q4_0_DECODE, chk)
+    torch.cuda.synchronize()

@@ -118,6 +118,17 @@ def test_accept_argument_checks(L):
     assert tv.tv_accept_workspace_bytes(3, 0) == 0
 
 
+def test_stream_probe_argument_checks(L):
+    f = L.tv_stream_probe
+    assert f(None, 4096, 0, 4096, 8, None) == -1
+    assert f(4096, 4096, 0, None, 8, None) == -1
+    assert f(4096, 4096, 2, 4096, 8, None) == -1       # unknown kind
+    assert f(4096, 0, 0, 4096, 8, None) == -3           # nothing to read
+    assert f(4096, 4096, 0, 4096, 0, None) == -3        # no workgroup
+    assert f(4096, 4100, 1, 4096, 8, None) == -4        # not a multiple of 16 bytes
+    assert f(4104, 4096, 1, 4096, 8, None) == -4        # base not 16-byte aligned
+
+
 def test_library_links_no_oracle():
     """The GPU library and the oracle share nothing: no oracle symbol, no
     oracle header."""

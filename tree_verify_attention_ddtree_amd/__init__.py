@@ -108,6 +108,8 @@ def lib():
         L.tree_commit_kv_layers.restype = ctypes.c_int
         L.tree_accept_noalloc.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
         L.tree_accept_noalloc.restype = ctypes.c_int
+        L.tv_stream_probe.argtypes = [P, ctypes.c_uint64, ctypes.c_int32, P, ctypes.c_int32, P]
+        L.tv_stream_probe.restype = ctypes.c_int
         L.tv_attn_plan.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.POINTER(TvAttnPlanInfo)]
         L.tv_attn_plan.restype = ctypes.c_int
         _lib = L
@@ -128,7 +130,7 @@ class TvCommitDesc(ctypes.Structure):
 
 
 EXPORTS = ("tree_verify_attn", "tree_accept", "tree_commit_kv", "tree_commit_kv_layers", "tv_attn_workspace_bytes",
-           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan", "tree_accept_noalloc")
+           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan", "tree_accept_noalloc", "tv_stream_probe")
 
 
 def tv_strerror(code: int) -> str:
@@ -241,6 +243,21 @@ def tree_accept_noalloc(logits, parent, tokens, argmax_out, result_out, stream=N
                                    _stream_ptr(stream))
     if rc != TV_OK:
         raise TvError(rc, "tree_accept_noalloc")
+
+
+TV_PROBE_READ = 0
+TV_PROBE_Q4_0_DECODE = 1
+
+
+def tv_stream_probe(buf, kind, checksums, stream=None) -> None:
+    """Stream a device tensor's bytes (read, or read and unpack as Q4_0
+    codes) with one checksum word per workgroup in ``checksums`` (device
+    uint32/int32 tensor; its length is the workgroup count)."""
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib().tv_stream_probe(_ptr(buf), nbytes, int(kind), _ptr(checksums), int(checksums.numel()),
+                               _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tv_stream_probe")
 
 
 def make_commit_desc(n_nodes, n_kv_heads, head_dim, kv_type, n_ctx, capacity, kv_token_stride, kv_head_stride):

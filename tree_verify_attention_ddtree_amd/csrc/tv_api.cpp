@@ -18,6 +18,8 @@ int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, 
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
 int launch_accept_noalloc(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                           int32_t *argmax_out, int32_t *result_out, hipStream_t stream);
+int launch_stream_probe(const void *buf, uint64_t bytes, int kind, uint32_t *checksums, int n_wg,
+                        hipStream_t stream);
 int launch_commit(const tv_commit_desc *d, int n_layers, const int32_t *result, const void *const *k_tree,
                   const void *const *v_tree, void *const *k_cache, void *const *v_cache, hipStream_t stream);
 
@@ -317,6 +319,16 @@ int tree_accept_noalloc(const float *logits, int32_t n_nodes, int32_t vocab, con
     if (rc) return rc;
     return tv::launch_accept_noalloc(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out,
                                      (hipStream_t)stream);
+}
+
+int tv_stream_probe(const void *buf, uint64_t bytes, int32_t kind, uint32_t *checksums, int32_t n_checksums,
+                    void *stream)
+{
+    if (!buf || !checksums) return TV_E_ARG;
+    if (kind != TV_PROBE_READ && kind != TV_PROBE_Q4_0_DECODE) return TV_E_ARG;
+    if (bytes == 0 || n_checksums < 1 || n_checksums > (1 << 20)) return TV_E_SHAPE;
+    if (bytes % 16 || !aligned(buf, 16) || !aligned(checksums, 4)) return TV_E_ALIGN;
+    return tv::launch_stream_probe(buf, bytes, kind, checksums, n_checksums, (hipStream_t)stream);
 }
 
 static int check_commit_desc(const tv_commit_desc *d)
