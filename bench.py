@@ -122,6 +122,15 @@ def timed(torch, stream, fn, k):
     return e0.elapsed_time(e1) / k
 
 
+def timed_median(torch, stream, fn, k, parts=6):
+    """Median over `parts` back-to-back runs of k / parts calls each of the
+    average ms per call: a stall outside the kernels (seen once in a while on
+    a freshly allocated gigabyte, tens of ms in one run) moves one part, not
+    the figure."""
+    per = max(1, k // parts)
+    return float(np.median([timed(torch, stream, lambda i, j=j: fn(j * per + i), per) for j in range(parts)]))
+
+
 def rotated_q4_0(torch, dev, n_kv, rows, row_bytes, seed):
     """A head-major Q4_0 cache [n_kv, rows, row_bytes] drawn on the device:
     block scales fp16(|N(0,1)| * 0.05), uniform code bytes (the distribution
@@ -209,7 +218,7 @@ def layer_config(torch, tv, dev, stream, name, Hq, Hkv, D, T, W, kv, parent, win
         tv.tree_verify_attn(desc, kc[:, off:], vc[:, off:], q, kt, vt, out, ws, wsb, stream)
 
     timed(torch, stream, launch, 50)
-    ms = timed(torch, stream, launch, launches)
+    ms = timed_median(torch, stream, launch, launches)
     rec = attn_record(ms * 1e3, 2 * Hkv * R * row_bytes, 4.0 * Hq * n * R * D)
     rec.update({"n_ctx": T, "window": W, "window_mode": window_mode, "kv": kv, "n_nodes": n,
                 "heads": f"{Hq}/{Hkv}", "head_dim": D, "kv_views_rotated": n_views, "launches_timed": launches,
@@ -231,7 +240,7 @@ def stream_probes(torch, tv, stream, caches, kv_bytes):
             tv.tv_stream_probe(kc, kind, chk, stream)
             tv.tv_stream_probe(vc, kind, chk, stream)
         timed(torch, stream, probe, 20)
-        ms = timed(torch, stream, probe, 200)
+        ms = timed_median(torch, stream, probe, 200)
         gbps = kv_bytes / (ms * 1e-3) / 1e9
         out[name] = {"us": ms * 1e3, "gbps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     out["bytes_per_call"] = kv_bytes
@@ -283,42 +292,69 @@ def full_step(torch, tv, synth, dev, stream, passes):
     k_trees = [[t["qkv"][tr]["k_tree"] for t in layers] for tr in range(ntr)]
     v_trees = [[t["qkv"][tr]["v_tree"] for t in layers] for tr in range(ntr)]
 
-    def one_step(i):
+    # the one-launch form: every layer's output kept, one work-queue launch
+    step_outs = [torch.empty((23, Hq, D), dtype=torch.float32, device=dev) for _ in range(L)]
+    step_layers = [tv.step_layers([(t["k_cache"], t["v_cache"], t["qkv"][tr]["q"], t["qkv"][tr]["k_tree"],
+                                    t["qkv"][tr]["v_tree"], o) for t, o in zip(layers, step_outs)])
+                   for tr in range(ntr)]
+    sws = torch.zeros(max(tv.tv_step_workspace_bytes(d, L, w["vocab"]) for d, _ in descs), dtype=torch.uint8,
+                      device=dev)
+    splan = tv.tv_step_plan(descs[0][0], L, w["vocab"])
+
+    def one_step(i, single):
         tr = i % ntr
         d, _p = descs[tr]
-        for t in layers:
-            x = t["qkv"][tr]
-            tv.tree_verify_attn(d, t["k_cache"], t["v_cache"], x["q"], x["k_tree"], x["v_tree"], outs, ws, wsb,
-                                stream)
-        tv.tree_accept(logits[tr], trees[tr]["parent"], trees[tr]["tokens"], am, res[tr], aws, stream)
+        if single:
+            tv.tree_verify_step(d, step_layers[tr], logits[tr], trees[tr]["tokens"], am, res[tr], sws, stream)
+        else:
+            for t in layers:
+                x = t["qkv"][tr]
+                tv.tree_verify_attn(d, t["k_cache"], t["v_cache"], x["q"], x["k_tree"], x["v_tree"], outs, ws, wsb,
+                                    stream)
+            tv.tree_accept(logits[tr], trees[tr]["parent"], trees[tr]["tokens"], am, res[tr], aws, stream)
         tv.tree_commit_kv_layers(cdesc, res[tr], k_trees[tr], v_trees[tr], k_caches, v_caches, stream)
 
-    for i in range(8):
-        one_step(i)
-    torch.cuda.synchronize()
-    steps = passes * ntr
-    pipelined_ms = timed(torch, stream, one_step, steps)
-    got = res.cpu().numpy()
-    accepted_ok = all(int(got[tr][0]) == trees[tr]["n_acc"] for tr in range(ntr))
-    t0 = time.perf_counter()
-    for i in range(ntr):
-        one_step(i)
-        host.copy_(res[i % ntr], non_blocking=True)
-        stream.synchronize()
-        accepted_ok = accepted_ok and int(host[0]) == trees[i % ntr]["n_acc"]
-    synced_ms = (time.perf_counter() - t0) * 1e3 / ntr
     kv_step = L * 2 * Hkv * T * 144
     rec = {
         "workload": "16 layers x (24 q / 4 kv heads, head_dim 256, 32768 Q4_0 rows), 64 seeded budget-22 trees "
                     "(one per step, shared by all layers), acceptance over 23x152000 logits, KV commit of the "
                     "accepted path into the 16 layers (one launch)",
-        "steps_timed_pipelined": steps, "steps_per_s_pipelined": 1e3 / pipelined_ms,
-        "ms_per_step_pipelined": pipelined_ms, "steps_per_s_with_host_sync": 1e3 / synced_ms,
-        "ms_per_step_with_host_sync": synced_ms, "kv_gbps": kv_step / (pipelined_ms * 1e-3) / 1e9,
-        "accepted_lengths_match_planted": bool(accepted_ok),
+        "one_launch_plan": splan,
     }
-    log(f"full step: {pipelined_ms:.3f} ms pipelined, {synced_ms:.3f} ms with host sync")
-    del layers, logits
+    accepted_ok = True
+    for single in (True, False):
+        for i in range(8):
+            one_step(i, single)
+        torch.cuda.synchronize()
+        steps = passes * ntr
+        res.fill_(-1)
+        pipelined_ms = timed(torch, stream, lambda i: one_step(i, single), steps)
+        got = res.cpu().numpy()
+        ok = all(int(got[tr][0]) == trees[tr]["n_acc"] for tr in range(ntr))
+        t0 = time.perf_counter()
+        for i in range(ntr):
+            one_step(i, single)
+            host.copy_(res[i % ntr], non_blocking=True)
+            stream.synchronize()
+            ok = ok and int(host[0]) == trees[i % ntr]["n_acc"]
+        synced_ms = (time.perf_counter() - t0) * 1e3 / ntr
+        accepted_ok = accepted_ok and ok
+        form = {"steps_timed_pipelined": steps, "steps_per_s_pipelined": 1e3 / pipelined_ms,
+                "ms_per_step_pipelined": pipelined_ms, "steps_per_s_with_host_sync": 1e3 / synced_ms,
+                "ms_per_step_with_host_sync": synced_ms, "kv_gbps": kv_step / (pipelined_ms * 1e-3) / 1e9,
+                "accepted_lengths_match_planted": bool(ok)}
+        if single:
+            # the step and the commit: two launches
+            form["launches_per_step"] = splan["launches"] + 1
+            rec.update(form)
+            rec["attention_and_acceptance"] = "tree_verify_step (work-queue kernel, one launch)"
+        else:
+            form["launches_per_step"] = 2 * L + 2
+            rec["separate_launches"] = form
+        log(f"full step ({'one launch' if single else 'separate launches'}): {pipelined_ms:.3f} ms pipelined, "
+            f"{synced_ms:.3f} ms with host sync")
+    rec["accepted_lengths_match_planted"] = bool(accepted_ok)
+    del layers, logits, step_outs, step_layers, sws
     torch.cuda.empty_cache()
     return rec, trees
 
@@ -419,10 +455,10 @@ def main():
                                                             24, 4, 256, 61440, 2048, "q4_0", p61, window_mode=1,
                                                             seed=42)
         timed(torch, stream, attn, 50)
-        ms_tree = timed(torch, stream, attn, 500)
+        ms_tree = timed_median(torch, stream, attn, 500)
         cfg["long_128k_tree"] = attn_record(ms_tree * 1e3, kv_bytes, flops)
         cfg["long_128k_tree"].update({"n_ctx": T, "n_nodes": n, "kv": "q4_0", "kv_copies_rotated": n_copies})
-        ms_chain = timed(torch, stream, lambda i: tv.tree_verify_attn(
+        ms_chain = timed_median(torch, stream, lambda i: tv.tree_verify_attn(
             cdesc, caches[i % n_copies][0], caches[i % n_copies][1], cq, ckt, cvt, cout, cws, None, stream), 500)
         cfg["long_128k_chain16"] = attn_record(ms_chain * 1e3, kv_bytes, 4.0 * Hq * 16 * R * D)
         cfg["long_128k_chain16"].update({"n_ctx": T, "n_nodes": 16, "kv": "q4_0", "kv_copies_rotated": n_copies})
@@ -438,8 +474,8 @@ def main():
     torch.cuda.synchronize()
     ms_step = timed(torch, stream, step, args.steps)
     # the two parts of a step on their own (same stream, same rotation)
-    ms_attn = timed(torch, stream, attn, max(args.steps, 200))
-    ms_accept = timed(torch, stream, lambda i: accept(), max(args.steps, 200))
+    ms_attn = timed_median(torch, stream, attn, max(args.steps, 300))
+    ms_accept = timed_median(torch, stream, lambda i: accept(), max(args.steps, 300))
     assert int(res[0].item()) == planted_L
     log(f"headline: {ms_step * 1e3:.1f} us per step, attention {ms_attn * 1e3:.1f} us")
 

@@ -326,6 +326,71 @@ TV_API int tree_commit_kv_layers(const tv_commit_desc *d, int32_t n_layers, cons
                           const void *const *k_tree, const void *const *v_tree, void *const *k_cache,
                           void *const *v_cache, void *stream);
 
+/* Layers one tree_verify_step call takes. */
+#define TV_MAX_LAYERS 16
+
+/*
+ * Device workspace (bytes) of tree_verify_step for n_layers layers of shape
+ * `d` and `vocab` logits per node: a 2048-byte work-queue header (counters,
+ * a status word and the acceptance state), then per layer one block of split
+ * partials of tv_attn_workspace_bytes(d) bytes rounded up to a multiple of
+ * 256. 0 when d is invalid, n_layers is outside 1..TV_MAX_LAYERS or
+ * vocab < 1.
+ */
+TV_API size_t tv_step_workspace_bytes(const tv_attn_desc *d, int32_t n_layers, int32_t vocab);
+
+/* How tree_verify_step runs a shape (host only, launches nothing). */
+typedef struct tv_step_plan_info {
+    int32_t launches;   /* kernel launches per call: 1 with the work-queue kernel */
+    int32_t workgroups; /* workgroups of the work-queue kernel, 0 without it */
+    int64_t items;      /* its work items: acceptance, split and merge items */
+    uint64_t workspace_bytes;
+} tv_step_plan_info;
+
+/* n_cu <= 0 asks the current device for its compute-unit count. */
+TV_API int tv_step_plan(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, int32_t n_cu,
+                        tv_step_plan_info *out);
+
+/*
+ * One verify step over n_layers attention layers and the acceptance,
+ * asynchronous on `stream`. Results equal, bit for bit, those of
+ * tree_verify_attn(d, &layers[l], ...) for l = 0 .. n_layers-1 followed by
+ * tree_accept(logits, d->n_nodes, vocab, d->parent, tokens, argmax_out,
+ * result_out, ...), with the same checks and error codes.
+ *
+ * d           one descriptor for every layer (tree, heads, head_dim, context,
+ *             window, scale, cache type and strides).
+ * layers      HOST array of n_layers (1..TV_MAX_LAYERS) tensor sets, each as
+ *             in tree_verify_attn.
+ * logits, vocab, tokens, argmax_out, result_out   as in tree_accept; the
+ *             logits are an input of the step, so a caller whose logits
+ *             depend on these layers' outputs calls tree_verify_attn per
+ *             layer instead.
+ * workspace   device, tv_step_workspace_bytes(d, n_layers, vocab) bytes,
+ *             256-byte aligned; its first 2048 bytes all zero before the
+ *             first call (e.g. zeroed once when allocated). Every call leaves
+ *             them zero again, except the status word (uint32 at byte 8),
+ *             which a call sets to 1 if a merge item's wait ever ran out
+ *             (not expected to happen: that call's outputs are then not
+ *             valid) and which only the caller clears. Calls that share a
+ *             workspace must not overlap.
+ *
+ * Where the plan's split kernel is TV_SPLIT_Q4_0_WS the step is one launch
+ * of a persistent kernel (at most one workgroup per compute unit) that takes
+ * work items from a device-side queue in ticket order: the acceptance
+ * slices, then every layer's split items, each layer's merge items queued
+ * behind the next layer's splits. A merge item waits (a bounded spin) for
+ * its layer's split items, which hold lower tickets and so are already
+ * running or done: no wait depends on a workgroup that has not started.
+ * Other plans make the same launches as the separate calls, in order on
+ * `stream`. The persistent kernel is the idea of "We got 207 tok/s with
+ * Qwen3.5-27B on an RTX 3090", "What makes it work" (one kernel instead of
+ * many launches per token).
+ */
+TV_API int tree_verify_step(const tv_attn_desc *d, int32_t n_layers, const tv_attn_ptrs *layers,
+                            const float *logits, int32_t vocab, const int32_t *tokens, int32_t *argmax_out,
+                            int32_t *result_out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Kinds of tv_stream_probe. */
 #define TV_PROBE_READ 0        /* read every byte */
 #define TV_PROBE_Q4_0_DECODE 1 /* read, and unpack every byte as Q4_0 codes times a scale */

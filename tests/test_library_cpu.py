@@ -252,3 +252,63 @@ def test_plan_without_splits_needs_no_workspace(n_ctx):
         p = _plan(24, 4, 23, 256, kv, n_ctx)
         assert p["splits"] == 0 and p["workspace_bytes"] == 0 and p["kernel"] == tv.TV_SPLIT_NONE
         assert p["merge_rows"] == n_ctx
+
+
+def test_step_argument_checks(L):
+    """tree_verify_step rejects bad arguments on the host, before it asks the
+    device anything (so nothing here launches where a GPU is visible)."""
+    d, keep = _desc(parent=(-1, 0, 1), Hq=24, Hkv=4, D=256, n_ctx=4096, ts=144, hs=144 * 4096)
+    good = tv.TvAttnPtrs(4096, 4096, 4096, 4096, 4096, 4096)
+    arr = (tv.TvAttnPtrs * 2)(good, good)
+    tok = np.array([0, 1, 2], np.int32)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    f = lambda dd, nl, ly, lg=4096, V=100, tk=P(tok), am=4096, res=4096, ws=4096: L.tree_verify_step(
+        ctypes.byref(dd), nl, ly, lg, V, tk, am, res, ws, 1 << 40, None)
+    assert f(d, 0, arr) == -3                      # no layer
+    assert f(d, tv.TV_MAX_LAYERS + 1, arr) == -3   # too many layers
+    assert f(d, 2, None) == -1
+    bad = (tv.TvAttnPtrs * 2)(good, tv.TvAttnPtrs(4096, 4096, None, 4096, 4096, 4096))
+    assert f(d, 2, bad) == -1                      # a null tensor in the second layer
+    bad = (tv.TvAttnPtrs * 2)(good, tv.TvAttnPtrs(4096, 4096, 4096, 4096, 4100, 4096))
+    assert f(d, 2, bad) == -4                      # a misaligned one
+    assert f(d, 2, arr, lg=None) == -1
+    assert f(d, 2, arr, V=0) == -3
+    assert f(d, 2, arr, tk=None) == -1
+    assert f(d, 2, arr, ws=None) == -5
+    assert f(d, 2, arr, ws=4096 + 16) == -4        # the workspace is 256-byte aligned
+    dt, keep2 = _desc(parent=(-1, 0, 2), Hq=24, Hkv=4, D=256, n_ctx=4096, ts=144, hs=144 * 4096)
+    assert f(dt, 2, arr) == -2
+    assert L.tree_verify_step(None, 1, arr, 4096, 10, P(tok), 4096, 4096, 4096, 1 << 20, None) == -1
+
+
+def test_step_plan():
+    """One launch where the warp-specialised split kernel runs: one work item
+    per workgroup (acceptance items of two 8192-logit slices, split items,
+    merge items of 8 rows, 4 for the last layer); the separate launches
+    otherwise. The workspace is
+    a 2048-byte header plus each layer's partials, rounded to 256 bytes."""
+    Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
+    par = [-1] + [i // 2 for i in range(22)]
+
+    def plan(kv, n_ctx, L, vocab, D=256, parent=par, window=0):
+        row = D // 32 * 18 if kv == Q else 2 * D
+        d, keep = tv.make_desc(parent, 24, 4, D, kv, n_ctx, window, 0.0625, row, row * max(n_ctx, 1))
+        return tv.tv_step_plan(d, L, vocab, 256), tv.tv_attn_plan(d, 256)
+
+    p, a = plan(Q, 32768, 16, 152000)
+    assert a["kernel"] == tv.TV_SPLIT_Q4_0_WS and a["splits"] == 64
+    n_items = (23 * 19 + 1) // 2 + 16 * 64 * 4 + 15 * ((23 * 24 + 7) // 8) + (23 * 24 + 3) // 4
+    assert (p["launches"], p["workgroups"], p["items"]) == (1, n_items, n_items)
+    assert p["workspace_bytes"] == 2048 + 16 * ((a["workspace_bytes"] + 255) // 256 * 256)
+    # a 2048-row window: two row groups per KV head
+    p, a = plan(Q, 61440, 3, 1000, window=2048)
+    assert a["row_groups"] == 2 and p["items"] == (23 + 1) // 2 + 3 * 32 * 4 * 2 + 2 * 69 + 138
+    # separate launches: F16, head_dim 128, no whole chunk, a masked plan
+    for kv, n_ctx, D in ((F, 32768, 256), (Q, 32768, 128), (Q, 50, 256), (Q, 4096 + 37, 256)):
+        p, a = plan(kv, n_ctx, 4, 1000, D=D)
+        assert p["workgroups"] == 0 and p["items"] == 0
+        assert p["launches"] == 4 * (2 if a["splits"] else 1) + 1
+    with pytest.raises(tv.TvError):
+        plan(Q, 32768, 0, 1000)
+    with pytest.raises(tv.TvError):
+        plan(Q, 32768, 2, 0)

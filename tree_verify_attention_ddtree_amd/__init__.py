@@ -22,6 +22,7 @@ TV_OK = 0
 TV_KV_F16 = 0
 TV_KV_Q4_0 = 1
 TV_MAX_NODES = 64
+TV_MAX_LAYERS = 16
 
 _lib = None
 
@@ -74,6 +75,15 @@ TV_SPLIT_Q4_0 = 2
 TV_SPLIT_Q4_0_WS = 3
 
 
+class TvStepPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("launches", ctypes.c_int32),
+        ("workgroups", ctypes.c_int32),
+        ("items", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
 class TvError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
@@ -112,6 +122,14 @@ def lib():
         L.tv_stream_probe.restype = ctypes.c_int
         L.tv_attn_plan.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.POINTER(TvAttnPlanInfo)]
         L.tv_attn_plan.restype = ctypes.c_int
+        L.tv_step_workspace_bytes.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.c_int32]
+        L.tv_step_workspace_bytes.restype = ctypes.c_size_t
+        L.tv_step_plan.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(TvStepPlanInfo)]
+        L.tv_step_plan.restype = ctypes.c_int
+        L.tree_verify_step.argtypes = [ctypes.POINTER(TvAttnDesc), ctypes.c_int32, ctypes.POINTER(TvAttnPtrs), P,
+                                       ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P]
+        L.tree_verify_step.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -130,7 +148,8 @@ class TvCommitDesc(ctypes.Structure):
 
 
 EXPORTS = ("tree_verify_attn", "tree_accept", "tree_commit_kv", "tree_commit_kv_layers", "tv_attn_workspace_bytes",
-           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan", "tree_accept_noalloc", "tv_stream_probe")
+           "tv_accept_workspace_bytes", "tv_strerror", "tv_attn_plan", "tree_accept_noalloc", "tv_stream_probe",
+           "tv_step_workspace_bytes", "tv_step_plan", "tree_verify_step")
 
 
 def tv_strerror(code: int) -> str:
@@ -203,6 +222,58 @@ def tree_verify_attn(desc: TvAttnDesc, k_cache, v_cache, q, k_tree, v_tree, out,
                                 _stream_ptr(stream))
     if rc != TV_OK:
         raise TvError(rc, "tree_verify_attn")
+
+
+def _attn_ptrs(k_cache, v_cache, q, k_tree, v_tree, out):
+    return TvAttnPtrs(*(p.value if p is not None else None for p in
+                        (_ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out))))
+
+
+def tv_step_workspace_bytes(desc: TvAttnDesc, n_layers: int, vocab: int) -> int:
+    return int(lib().tv_step_workspace_bytes(ctypes.byref(desc), int(n_layers), int(vocab)))
+
+
+def tv_step_plan(desc: TvAttnDesc, n_layers: int, vocab: int, n_cu: int = 0) -> dict:
+    """How tree_verify_step runs this shape (host only): launches per call,
+    work-queue workgroups and items, workspace bytes."""
+    info = TvStepPlanInfo()
+    rc = lib().tv_step_plan(ctypes.byref(desc), int(n_layers), int(vocab), int(n_cu), ctypes.byref(info))
+    if rc != TV_OK:
+        raise TvError(rc, "tv_step_plan")
+    return {name: int(getattr(info, name)) for name, _ in TvStepPlanInfo._fields_}
+
+
+def step_layers(layers):
+    """The C array of per-layer tensors tree_verify_step takes, from a
+    sequence of (k_cache, v_cache, q, k_tree, v_tree, out) device tensors
+    (build it once to call the step many times)."""
+    arr = (TvAttnPtrs * max(1, len(layers)))()
+    for i, ly in enumerate(layers):
+        arr[i] = _attn_ptrs(*ly)
+    return arr
+
+
+def tree_verify_step(desc: TvAttnDesc, layers, logits, tokens, argmax_out, result_out, workspace,
+                     stream=None) -> None:
+    """One verify step (see include/tree_verify.h): ``layers`` is a sequence
+    of (k_cache, v_cache, q, k_tree, v_tree, out) device tensors, one per
+    layer, all of the descriptor's shape (or the array step_layers made of
+    one); ``logits`` device fp32
+    [n, vocab]; ``tokens`` a host int sequence (the parent array is the
+    descriptor's); ``workspace`` a device tensor of
+    tv_step_workspace_bytes(desc, len(layers), vocab) bytes whose first 2048
+    bytes are zero before its first use (allocate it with torch.zeros)."""
+    n, vocab = int(logits.shape[0]), int(logits.shape[1])
+    tok = np.ascontiguousarray(np.asarray(tokens), dtype=np.int32)
+    if len(tok) != n or n != desc.n_nodes:
+        raise ValueError("tokens length and logits.shape[0] must equal the descriptor's node count")
+    arr = step_layers(layers) if not isinstance(layers, ctypes.Array) else layers
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().tree_verify_step(ctypes.byref(desc), len(layers), arr, _ptr(logits), vocab,
+                                tok.ctypes.data_as(ctypes.c_void_p), _ptr(argmax_out), _ptr(result_out),
+                                _ptr(workspace), int(wsb), _stream_ptr(stream))
+    if rc != TV_OK:
+        raise TvError(rc, "tree_verify_step")
 
 
 def tv_accept_workspace_bytes(n_nodes: int, vocab: int) -> int:

@@ -20,6 +20,12 @@ int launch_accept_noalloc(const float *logits, int n, int vocab, const int32_t *
                           int32_t *argmax_out, int32_t *result_out, hipStream_t stream);
 int launch_stream_probe(const void *buf, uint64_t bytes, int kind, uint32_t *checksums, int n_wg,
                         hipStream_t stream);
+size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers);
+void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int n_cu, int *launches,
+                int *workgroups, int64_t *items);
+int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers, const float *logits, int vocab,
+                const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *ws, int n_cu,
+                const SplitPlan &plan, hipStream_t stream);
 int launch_commit(const tv_commit_desc *d, int n_layers, const int32_t *result, const void *const *k_tree,
                   const void *const *v_tree, void *const *k_cache, void *const *v_cache, hipStream_t stream);
 
@@ -261,16 +267,23 @@ int tv_attn_plan(const tv_attn_desc *d, int32_t n_cu, tv_attn_plan_info *out)
     return TV_OK;
 }
 
-int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
-                     void *stream)
+static int check_ptrs(const tv_attn_desc *d, const tv_attn_ptrs *p)
 {
-    int rc = tv::check_desc(d);
-    if (rc) return rc;
     if (!p || !p->q || !p->k_tree || !p->v_tree || !p->out) return TV_E_ARG;
     if (d->n_ctx > 0 && (!p->k_cache || !p->v_cache)) return TV_E_ARG;
     if (!aligned(p->q, 16) || !aligned(p->k_tree, 16) || !aligned(p->v_tree, 16) || !aligned(p->out, 16))
         return TV_E_ALIGN;
     if (d->n_ctx > 0 && (!aligned(p->k_cache, 16) || !aligned(p->v_cache, 16))) return TV_E_ALIGN;
+    return TV_OK;
+}
+
+int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    int rc = tv::check_desc(d);
+    if (rc) return rc;
+    rc = check_ptrs(d, p);
+    if (rc) return rc;
     int n_cu = 0;
     rc = tv::device_cu_count(&n_cu);
     if (rc) return rc;
@@ -319,6 +332,71 @@ int tree_accept_noalloc(const float *logits, int32_t n_nodes, int32_t vocab, con
     if (rc) return rc;
     return tv::launch_accept_noalloc(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out,
                                      (hipStream_t)stream);
+}
+
+static int step_setup(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, int32_t n_cu_in, int *n_cu,
+                      tv::SplitPlan *plan)
+{
+    int rc = tv::check_desc(d);
+    if (rc) return rc;
+    if (n_layers < 1 || n_layers > TV_MAX_LAYERS || vocab < 1) return TV_E_SHAPE;
+    *n_cu = n_cu_in;
+    if (*n_cu <= 0) {
+        rc = tv::device_cu_count(n_cu);
+        if (rc) return rc;
+    }
+    return tv::plan_attn(d, *n_cu, plan);
+}
+
+size_t tv_step_workspace_bytes(const tv_attn_desc *d, int32_t n_layers, int32_t vocab)
+{
+    int n_cu = 0;
+    tv::SplitPlan plan;
+    if (step_setup(d, n_layers, vocab, 0, &n_cu, &plan)) return 0;
+    return tv::step_ws_bytes(d, plan, n_layers);
+}
+
+int tv_step_plan(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, int32_t n_cu, tv_step_plan_info *out)
+{
+    int cu = 0;
+    tv::SplitPlan plan;
+    int rc = step_setup(d, n_layers, vocab, n_cu, &cu, &plan);
+    if (rc) return rc;
+    if (!out) return TV_E_ARG;
+    memset(out, 0, sizeof(*out));
+    int launches = 0, wgs = 0;
+    int64_t items = 0;
+    tv::step_shape(d, plan, n_layers, vocab, cu, &launches, &wgs, &items);
+    out->launches = launches;
+    out->workgroups = wgs;
+    out->items = items;
+    out->workspace_bytes = tv::step_ws_bytes(d, plan, n_layers);
+    return TV_OK;
+}
+
+int tree_verify_step(const tv_attn_desc *d, int32_t n_layers, const tv_attn_ptrs *layers, const float *logits,
+                     int32_t vocab, const int32_t *tokens, int32_t *argmax_out, int32_t *result_out,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = tv::check_desc(d);
+    if (rc) return rc;
+    if (n_layers < 1 || n_layers > TV_MAX_LAYERS) return TV_E_SHAPE;
+    if (!layers) return TV_E_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        rc = check_ptrs(d, &layers[l]);
+        if (rc) return rc;
+    }
+    rc = check_accept(logits, d->n_nodes, vocab, d->parent, tokens, argmax_out, result_out);
+    if (rc) return rc;
+    if (!workspace) return TV_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return TV_E_ALIGN;
+    int n_cu = 0;
+    tv::SplitPlan plan;
+    rc = step_setup(d, n_layers, vocab, 0, &n_cu, &plan);
+    if (rc) return rc;
+    if (workspace_bytes < tv::step_ws_bytes(d, plan, n_layers)) return TV_E_WORKSPACE;
+    return tv::launch_step(d, n_layers, layers, logits, vocab, tokens, argmax_out, result_out, workspace, n_cu, plan,
+                           (hipStream_t)stream);
 }
 
 int tv_stream_probe(const void *buf, uint64_t bytes, int32_t kind, uint32_t *checksums, int32_t n_checksums,

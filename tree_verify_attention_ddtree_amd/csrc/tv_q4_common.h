@@ -108,11 +108,11 @@ struct Q4Loader {
     //      (36 contiguous bytes);
     //   V: keys 4 (lane & 15) .. + 3, half-block (block 2q + (lane >> 5),
     //      half (lane >> 4) & 1).
-    __device__ __forceinline__ void init_ws(const SplitArgs &a, int gkv, int q, int lane)
+    __device__ __forceinline__ void init_ws(const SplitArgs &a, const SplitPtrs &p, int gkv, int q, int lane)
     {
         static_assert(D == 256, "the warp-specialised mapping is for head_dim 256");
-        kbase = a.k_cache + (int64_t)gkv * a.head_stride;
-        vbase = a.v_cache + (int64_t)gkv * a.head_stride;
+        kbase = p.k_cache + (int64_t)gkv * a.head_stride;
+        vbase = p.v_cache + (int64_t)gkv * a.head_stride;
         tok_stride = a.tok_stride;
         chunk_bytes = (u32)(kChunk * a.tok_stride);
         kk = 16 * q + (lane & 15);

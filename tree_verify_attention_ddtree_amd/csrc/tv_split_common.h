@@ -27,6 +27,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, u32
 // a per-lane buffer offset that is always out of range
 constexpr u32 kOffNone = 0x80000000u;
 
+// Cache-policy bit of a buffer store (its aux operand) that makes the store
+// coherent at device scope (sc1 on gfx950): complete, it is visible to every
+// workgroup of the device, with no L2 write-back.
+constexpr int kCpolSc1 = 16;
+
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
 // loop to its top, which would need a register per fragment.
 #define TV_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -230,6 +235,20 @@ __device__ __forceinline__ void maybe_rescale(float mnew, float &m, float &l, f4
 struct SplitArgs;
 typedef void (*split_fn)(const SplitArgs);
 
+// threads of a warp-specialised split workgroup (8 wave64s)
+constexpr int kWsThreads = 512;
+
+// The tensors of one split launch that change from layer to layer (a
+// multi-layer launch passes one set per layer with the other SplitArgs
+// fields shared).
+struct SplitPtrs {
+    const uint8_t *k_cache;
+    const uint8_t *v_cache;
+    const _Float16 *q;
+    _Float16 *ws_o;
+    float *ws_m;
+};
+
 // Tiles of one row group. Own tile k of wave w is t0 + 4k + w, shared tile u
 // is t0 + 4*NOWN + u; tiles at or past t_end are padding (zero queries,
 // results dropped), so every wave runs the same instructions.
@@ -305,9 +324,11 @@ struct QStage {
     static_assert(NQ * RS * QSTR <= 2 * Stage<D, KVT>::ELEMS, "staged query rows fit both stages");
     u4v pc[NQ];
 
-    __device__ __forceinline__ void load(const SplitArgs &a, int gkv, int t0, int tid)
+    __device__ __forceinline__ void load(const SplitArgs &a, int gkv, int t0, int tid) { load(a, a.q, gkv, t0, tid); }
+
+    __device__ __forceinline__ void load(const SplitArgs &a, const _Float16 *q, int gkv, int t0, int tid)
     {
-        const __amdgpu_buffer_rsrc_t rq = raw_rsrc(a.q, (u32)a.NR * (u32)(2 * D));
+        const __amdgpu_buffer_rsrc_t rq = raw_rsrc(q, (u32)a.NR * (u32)(2 * D));
         RowWalk rw(a, gkv, 16 * t0 + tid / PR, RS, 2 * D);
         const u32 part = 16u * (u32)(tid % PR);
 #pragma unroll

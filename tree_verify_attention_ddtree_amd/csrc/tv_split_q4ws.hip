@@ -1,481 +1,17 @@
-// Warp-specialised split kernel for Q4_0 caches with head_dim 256 (gfx950).
-//
-// Method: every node of a DDTree draft tree attends to the committed Q4_0 KV
-// cache in one verify pass ("Luce DFlash: 単一RTX 3090で最大2倍のスループット
-// を目指すQwen3.6-27B", feature list: DDTree tree verify, Q4_0 KV up to about
-// 128K context; "We got 207 tok/s with Qwen3.5-27B on an RTX 3090", "What we
-// built vs what we didn't"). This kernel computes, for one key-range split
-// of one KV head, the partial softmax state of every packed query row over
-// the cache rows of that range; the merge kernel adds the tree ancestors and
-// combines the splits.
-//
-// Same decomposition as split_q4_kernel (the packed GQA-group x tree-node
-// query rows of a KV head cut into 16-row tiles; 64-key chunks, two LDS
-// stages; S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_f16 with fp32
-// accumulation; online softmax in the exp2 domain with a lazy rescale), but a
-// workgroup has eight wave64s in two roles, and waves w and w + 4 of a
-// workgroup run on the same SIMD:
-//
-//   math wave q (0..3)   owns query tiles t0 + q and t0 + 4 + q (NOWN of them):
-//                        Q fragments and O accumulators stay in its
-//                        registers; per chunk it runs the scores, the
-//                        softmax and the PV of those tiles and nothing else;
-//   load wave q (4..7)   moves the raw Q4_0 bytes of chunk c + 3 from HBM
-//                        into registers and dequantises chunk c + 1 into
-//                        the other LDS stage: keys 16q .. 16q + 15 of K over
-//                        all of D, and D-quarter q of V (rows 64q .. 64q + 63
-//                        of V^T) over all 64 keys. It also runs the NSH
-//                        shared tiles: their scores over key tile q of each
-//                        chunk and their PV over D-quarter q.
-//
-// Within one wave, an MFMA and the vector instructions of the dequantisation
-// and softmax mostly take turns. With the MFMAs in one wave and the
-// dequantisation in the other, the SIMD issues the load wave's vector
-// instructions while the math wave's MFMAs execute.
-//
-// One barrier per chunk. Iteration i (chunk c, stage st = i & 1):
-//   math q: S^T(c) from stage st (two halves of 32 keys, each followed by its
-//           softmax), then PV(c) from stage st;
-//   load q: shared tiles: the exchange of chunk c - 1 (rescale when a wave
-//           flagged one) and its PV from stage st ^ 1, V^T quarter q; scores
-//           of chunk c over key tile q from stage st, P quarter to the
-//           exchange buffer of parity st;
-//           dequantise chunk c + 1 into stage st ^ 1 (K rows 16q.., V^T rows
-//           64q..); request the raw bytes of chunk c + 3.
-// Every LDS region a load wave writes in iteration i (stage st ^ 1: K rows
-// 16q.., V^T rows 64q..) was last read by the math waves in iteration i - 1
-// (before the barrier) and by that load wave itself earlier in iteration i;
-// the math waves read it again only after the next barrier. The shared
-// tiles' exchange buffers alternate with the parity, as the stages do.
+// Warp-specialised split kernel for Q4_0 caches with head_dim 256 (gfx950):
+// one workgroup per (key-range split, KV head, row group); the body and its
+// design notes are in tv_split_q4ws.h.
 
-#include <type_traits>
-
-#include "tv_q4_common.h"
+#include "tv_split_q4ws.h"
 
 namespace tv {
-
-constexpr int kWsThreads = 512;
-
-template <int V>
-using ic = std::integral_constant<int, V>;
-
 
 template <int NOWN, int NSH>
 __global__ void __launch_bounds__(kWsThreads, 1) split_q4ws_kernel(const SplitArgs a)
 {
-    constexpr int D = 256;
-    // K rows at 544 bytes (an S^T fragment read meets no bank conflict),
-    // V^T rows at 160 bytes
-    using St = Stage<D, TV_KV_Q4_0, true, true>;
-    using L = Q4Loader<D, true, true>;
-    using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH, kWsThreads>;
-    constexpr int NB = St::NB;     // 32-value blocks per row
-    constexpr int NDT = D / 16;    // D tiles
-    constexpr int NDQ = NDT / 4;   // D tiles of a quarter
-    constexpr int NSX = NSH > 0 ? NSH : 1;
-    // the planner gives a wave at most three tile slots (own + shared)
-    static_assert(NOWN >= 1 && NOWN <= 2 && NSH >= 0 && NOWN + NSH <= kMaxSlots, "tile layouts of this kernel");
-    static_assert(16 * QS::NT * QS::QSTR <= 2 * St::ELEMS, "staged query rows fit both stages");
-
-    __shared__ __attribute__((aligned(16))) _Float16 lds[2 * St::ELEMS];
-    // shared tiles, by chunk parity: P^T fragments ([k-step][lane], 8 halves),
-    // the maximum each load wave's key tile was taken against, rescale flags
-    __shared__ __attribute__((aligned(16))) _Float16 psh[2][NSX][2 * 64 * 8];
-    __shared__ float shmax[2][NSX][4][16];
-    __shared__ __attribute__((aligned(16))) int shflag[2][4];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool math = wv < 4;
-    const int q = wv & 3;
-    const int col = lane & 15, grp = lane >> 4;
-    const int split = blockIdx.x, gkv = blockIdx.y, rg = blockIdx.z;
-
-    TileMap tm;
-    tm.init(a.M, rg, gridDim.z);
-    const int64_t c_begin = split_chunk_begin(a, split);
-    const int nch = (int)(split_chunk_begin(a, split + 1) - c_begin);  // >= 1
-    const u32 magic = 0x64006400u;
-    const __amdgpu_buffer_rsrc_t rwm = raw_rsrc(a.ws_m + (int64_t)split * a.NR, (u32)a.NR * 4u);
-
-    // query rows of the workgroup's tiles, requested first (from L2); the
-    // load waves request the first two chunks' cache bytes behind them
-    QS qrows;
-    qrows.load(a, gkv, tm.t0, tid);
-
-    if (math) {
-        // ------------------------------------------------------------ math
-        qrows.write_rows(tid, lds);
-        __syncthreads();
-        h8 qf[NOWN][NB];
-#pragma unroll
-        for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) qf[k][bb] = QS::frag(lds, 16 * (4 * k + q), col, grp, bb);
-        __syncthreads();
-        // Q fragments are only MFMA B operands: parked in AGPRs
-#pragma unroll
-        for (int k = 0; k < NOWN; ++k)
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) (void)qf[k][bb];
-
-        f4 o[NOWN][NDT];
-        float m[NOWN], l[NOWN];
-#pragma unroll
-        for (int k = 0; k < NOWN; ++k) {
-            m[k] = kNegBig;
-            l[k] = 0.f;
-#pragma unroll
-            for (int j = 0; j < NDT; ++j) o[k][j] = (f4){0.f, 0.f, 0.f, 0.f};
-        }
-
-        // One chunk in two halves of 32 keys (k-steps kk = 0, 1 of the PV):
-        // scores of key tiles 2kk and 2kk + 1, their softmax, then their PV
-        // over all of D, so that only one half's P fragments are live.
-        auto body = [&](auto stc, bool live) {
-            constexpr int st = decltype(stc)::value;
-            __syncthreads();
-            if (!live) return;
-            const _Float16 *ks = lds + st * St::ELEMS;
-            const _Float16 *vt = ks + St::KELEMS;
-            // K fragment ii of half kk: key tile 2kk + (ii & 1), block ii >> 1;
-            // V fragment j of half kk: D tile j, k-step kk
-            auto kfrag = [&](int kk, int ii) -> h8 {
-                return *(const h8 *)(ks + (16 * (2 * kk + (ii & 1)) + col) * St::KSTR + 32 * (ii >> 1) + 8 * grp);
-            };
-            auto vfrag = [&](int kk, int j) -> h8 {
-                return *(const h8 *)(vt + (16 * j + col) * St::VSTR + 32 * kk + 8 * grp);
-            };
-            // Each fragment read feeds NOWN MFMAs, so the four math waves
-            // keep the LDS busy: reads stream through 4-entry rings, three
-            // ahead of use, and run on across phases (the PV's first V
-            // fragments before the softmax, the next half's first K
-            // fragments during the PV's last MFMAs), so that the LDS does
-            // not idle while the softmax runs.
-            h8 kr[4];
-            kr[0] = kfrag(0, 0);
-            kr[1] = kfrag(0, 1);
-            kr[2] = kfrag(0, 2);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                // S^T over key tiles 2kk and 2kk + 1
-                f4 s[NOWN][2];
-#pragma unroll
-                for (int k = 0; k < NOWN; ++k) s[k][0] = s[k][1] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ii = 0; ii < 2 * NB; ++ii) {
-                    if (ii + 3 < 2 * NB) kr[(ii + 3) % 4] = kfrag(kk, ii + 3);
-#pragma unroll
-                    for (int k = 0; k < NOWN; ++k)
-                        s[k][ii & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[ii % 4], qf[k][ii >> 1], s[k][ii & 1],
-                                                                             0, 0, 0);
-                }
-                h8 vr[4];
-                vr[0] = vfrag(kk, 0);
-                vr[1] = vfrag(kk, 1);
-                vr[2] = vfrag(kk, 2);
-                TV_SCHED_FENCE();
-                // running maxima over these 32 keys; one wave-uniform
-                // branch for the rare rescale
-                float mnew[NOWN];
-                bool need = false;
-#pragma unroll
-                for (int k = 0; k < NOWN; ++k) {
-                    const float t0 = fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3]));
-                    const float t1 = fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3]));
-                    mnew[k] = xmax_16_32(fmaxf(t0, t1)) * a.c;
-                    need = need || (mnew[k] > m[k] + kTau);
-                }
-                if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-                    for (int k = 0; k < NOWN; ++k) {
-                        const float mm = fmaxf(m[k], mnew[k]);
-                        const float f = __builtin_amdgcn_exp2f(m[k] - mm);
-                        l[k] *= f;
-                        m[k] = mm;
-#pragma unroll
-                        for (int j = 0; j < NDT; ++j) o[k][j] *= f;
-                    }
-                }
-                // fp16 P^T fragment of k-step kk: elements 0..3 are keys
-                // 32kk + 4grp + (0..3), elements 4..7 keys 32kk + 16 + 4grp + (0..3)
-                h8 pf[NOWN];
-#pragma unroll
-                for (int k = 0; k < NOWN; ++k) {
-                    h2 p[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const f4 &sv = s[k][t >> 1];
-                        const int i0 = 2 * (t & 1);
-                        p[t] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0], a.c, -m[k])),
-                                      __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0 + 1], a.c, -m[k])));
-                    }
-                    l[k] += add_pair(p[0], add_pair(p[1], 0.f)) + add_pair(p[2], add_pair(p[3], 0.f));
-                    h8 fr;
-                    fr.s01 = p[0];
-                    fr.s23 = p[1];
-                    fr.s45 = p[2];
-                    fr.s67 = p[3];
-                    pf[k] = fr;
-                }
-                // O^T += V^T P^T over k-step kk
-#pragma unroll
-                for (int j = 0; j < NDT; ++j) {
-                    if (j + 3 < NDT)
-                        vr[(j + 3) % 4] = vfrag(kk, j + 3);
-                    else if (kk == 0)
-                        kr[j + 3 - NDT] = kfrag(1, j + 3 - NDT);
-#pragma unroll
-                    for (int k = 0; k < NOWN; ++k)
-                        o[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vr[j % 4], pf[k], o[k][j], 0, 0, 0);
-                }
-                TV_SCHED_FENCE();
-            }
-        };
-        for (int i = 0; i < nch; i += 2) {
-            body(ic<0>{}, true);
-            body(ic<1>{}, i + 1 < nch);
-        }
-        __syncthreads();  // E1: every wave is past the last chunk
-        __syncthreads();  // E2: the load waves' last PV has read its stage
-        // normalised fp16 rows into LDS, log2 denominators to the workspace
-#pragma unroll
-        for (int k = 0; k < NOWN; ++k) {
-            const float lt = wave_sum_16_32(l[k]);
-            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-            _Float16 *orow = lds + (16 * (4 * k + q) + col) * QS::QSTR + 4 * grp;
-#pragma unroll
-            for (int j = 0; j < NDT; ++j) *(h4 *)(orow + 16 * j) = __builtin_convertvector(o[k][j] * inv, h4);
-            const int tile = tm.t0 + 4 * k + q;
-            const int r = 16 * tile + col;
-            const bool writer = tile < tm.t_end && r < a.M && grp == 0;
-            const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(m[k], lt)), rwm,
-                                                  writer ? rowi * 4u : kOffNone, 0, 0);
-        }
-    } else {
-        // ------------------------------------------------------------ load
-        L ld0, ld1;  // raw bytes of even and odd chunks (relative to c_begin)
-        ld0.init_ws(a, gkv, q, lane);
-        ld1.init_ws(a, gkv, q, lane);
-        ld0.load_k_ws(chunk_row<false>(a, c_begin), true);
-        ld0.load_v(chunk_row<false>(a, c_begin), true);
-        ld1.load_k_ws(chunk_row<false>(a, c_begin + 1), 1 < nch);
-        ld1.load_v(chunk_row<false>(a, c_begin + 1), 1 < nch);
-        qrows.write_rows(tid, lds);
-        __syncthreads();
-        h8 qs[NSX][NB];
-#pragma unroll
-        for (int u = 0; u < NSH; ++u)
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) qs[u][bb] = QS::frag(lds, 16 * (4 * NOWN + u), col, grp, bb);
-        __syncthreads();
-        // chunk c_begin into stage 0; its raw registers then take chunk c_begin + 2
-#pragma unroll
-        for (int j = 0; j < NB; ++j) ld0.k_piece(j, lds, magic);
-#pragma unroll
-        for (int p = 0; p < L::V_PIECES; ++p) ld0.v_piece(p, lds + St::KELEMS, magic);
-        ld0.load_k_ws(chunk_row<false>(a, c_begin + 2), 2 < nch);
-        ld0.load_v(chunk_row<false>(a, c_begin + 2), 2 < nch);
-
-        f4 osh[NSX][NDQ];
-        float msh[NSX], lsh[NSX], mown[NSX];
-        h2 psv[NSX][2];
-#pragma unroll
-        for (int u = 0; u < NSX; ++u) {
-            msh[u] = kNegBig;
-            lsh[u] = 0.f;
-            mown[u] = kNegBig;
-            psv[u][0] = psv[u][1] = (h2){(_Float16)0.f, (_Float16)0.f};
-#pragma unroll
-            for (int j = 0; j < NDQ; ++j) osh[u][j] = (f4){0.f, 0.f, 0.f, 0.f};
-        }
-
-        // Shared tiles, the step after the chunk whose exchange has parity
-        // sp: if any load wave flagged that chunk, the running maximum moves
-        // to the largest of the four maxima its quarters were taken against
-        // and each quarter is scaled to it in fp16; this wave's own quarter
-        // (as used) goes into its row sums; then the PV of that chunk over
-        // D-quarter q from its stage.
-        auto shared_pv = [&](auto spc) {
-            constexpr int sp = decltype(spc)::value;
-            const u4v fl = *(const u4v *)shflag[sp];
-            h8 pfs[NSX][2];
-#pragma unroll
-            for (int u = 0; u < NSH; ++u) {
-                pfs[u][0] = *(const h8 *)(&psh[sp][u][0] + lane * 8);
-                pfs[u][1] = *(const h8 *)(&psh[sp][u][0] + (64 + lane) * 8);
-            }
-            if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
-#pragma unroll
-                for (int u = 0; u < NSH; ++u) {
-                    const float mw[4] = {shmax[sp][u][0][col], shmax[sp][u][1][col], shmax[sp][u][2][col],
-                                         shmax[sp][u][3][col]};
-                    const float mm = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-                    const float g = __builtin_amdgcn_exp2f(msh[u] - mm);
-                    lsh[u] *= g;
-                    msh[u] = mm;
-#pragma unroll
-                    for (int j = 0; j < NDQ; ++j) osh[u][j] *= g;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const h2 f = {(_Float16)__builtin_amdgcn_exp2f(mw[2 * kk] - mm),
-                                      (_Float16)__builtin_amdgcn_exp2f(mw[2 * kk + 1] - mm)};
-                        const h2 fa = {f.x, f.x}, fb = {f.y, f.y};
-                        pfs[u][kk].s01 *= fa;
-                        pfs[u][kk].s23 *= fa;
-                        pfs[u][kk].s45 *= fb;
-                        pfs[u][kk].s67 *= fb;
-                    }
-                    // the same fp16 products the other waves applied to this quarter
-                    const _Float16 fo = (_Float16)__builtin_amdgcn_exp2f(mown[u] - mm);
-                    const h2 fo2 = {fo, fo};
-                    psv[u][0] *= fo2;
-                    psv[u][1] *= fo2;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < NSH; ++u) lsh[u] += add_pair(psv[u][0], add_pair(psv[u][1], 0.f));
-            const _Float16 *vt = lds + sp * St::ELEMS + St::KELEMS;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int j = 0; j < NDQ; ++j) {
-                    const h8 vf = *(const h8 *)(vt + (16 * (NDQ * q + j) + col) * St::VSTR + 32 * kk + 8 * grp);
-#pragma unroll
-                    for (int u = 0; u < NSH; ++u)
-                        osh[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfs[u][kk], osh[u][j], 0, 0, 0);
-                }
-        };
-
-        auto body = [&](auto stc, int i) {
-            constexpr int st = decltype(stc)::value;
-            __syncthreads();
-            if (NSH > 0 && i < nch) {
-                if (i > 0) shared_pv(ic<st ^ 1>{});
-                // scores of key tile q of chunk c for the shared tiles
-                const _Float16 *kwb = lds + st * St::ELEMS + (16 * q + col) * St::KSTR + 8 * grp;
-                f4 ssh[NSX];
-#pragma unroll
-                for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int bb = 0; bb < NB; ++bb) {
-                    const h8 kw = *(const h8 *)(kwb + 32 * bb);
-#pragma unroll
-                    for (int u = 0; u < NSH; ++u)
-                        ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kw, qs[u][bb], ssh[u], 0, 0, 0);
-                }
-                // this wave's P^T quarter (k-step q / 2, elements 4 (q & 1) ..
-                // + 3) against the common running maximum or, when some row
-                // of the key tile exceeds it by more than kTau (the flag),
-                // against the larger of the two, so that no P exceeds 2^kTau
-                bool need_sh = false;
-                float mnew[NSX];
-#pragma unroll
-                for (int u = 0; u < NSH; ++u) {
-                    const float t = fmaxf(fmaxf(ssh[u][0], ssh[u][1]), fmaxf(ssh[u][2], ssh[u][3]));
-                    mnew[u] = xmax_16_32(t) * a.c;
-                    need_sh = need_sh || (mnew[u] > msh[u] + kTau);
-                }
-                const bool flag = __builtin_amdgcn_ballot_w64(need_sh) != 0;
-#pragma unroll
-                for (int u = 0; u < NSH; ++u) {
-                    const float mw = flag ? fmaxf(msh[u], mnew[u]) : msh[u];
-                    mown[u] = mw;
-                    psv[u][0] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][0], a.c, -mw)),
-                                       __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][1], a.c, -mw)));
-                    psv[u][1] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][2], a.c, -mw)),
-                                       __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][3], a.c, -mw)));
-                    h4 p4;
-                    p4.s01 = psv[u][0];
-                    p4.s23 = psv[u][1];
-                    *(h4 *)(&psh[st][u][0] + ((q >> 1) * 64 + lane) * 8 + 4 * (q & 1)) = p4;
-                    if (grp == 0) shmax[st][u][q][col] = mw;
-                }
-                if (lane == 0) shflag[st][q] = flag;
-            }
-            // dequantise chunk c + 1 (raw bytes of parity st ^ 1) into stage
-            // st ^ 1, then request chunk c + 3 into the same registers
-            _Float16 *ks_n = lds + (st ^ 1) * St::ELEMS;
-            auto next = [&](L &ldn) {
-                if (i + 1 < nch) {
-#pragma unroll
-                    for (int j = 0; j < NB; ++j) ldn.k_piece(j, ks_n, magic);
-#pragma unroll
-                    for (int p = 0; p < L::V_PIECES; ++p) ldn.v_piece(p, ks_n + St::KELEMS, magic);
-                }
-                ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
-                ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
-            };
-            if constexpr (st == 0)
-                next(ld1);
-            else
-                next(ld0);
-        };
-        // Both bodies run on every pass, the second past the last chunk too
-        // (then it only requests nothing through an empty descriptor and
-        // meets the barrier), so that every path through the loop issues
-        // the same loads in the same order and each wait counts only the
-        // chunk it needs: with an odd last pass skipped, the wait counts at
-        // the loop header had to cover both histories and waited for every
-        // load in flight.
-        for (int i = 0; i < nch; i += 2) {
-            body(ic<0>{}, i);
-            body(ic<1>{}, i + 1);
-        }
-        __syncthreads();  // E1: the last chunk's exchange is complete
-        // the last chunk's shared update and PV; this wave's row sums meet
-        // the other load waves' in the maxima buffer of the parity the last
-        // chunk did not use (all of its reads were before E1)
-        float(*shl)[4][16] = shmax[nch & 1];
-        if constexpr (NSH > 0) {
-            if ((nch - 1) & 1)
-                shared_pv(ic<1>{});
-            else
-                shared_pv(ic<0>{});
-#pragma unroll
-            for (int u = 0; u < NSH; ++u) {
-                const float lw = wave_sum_16_32(lsh[u]);
-                if (grp == 0) shl[u][q][col] = lw;
-            }
-        }
-        __syncthreads();  // E2
-#pragma unroll
-        for (int u = 0; u < NSH; ++u) {
-            const float lt = ((shl[u][0][col] + shl[u][1][col]) + shl[u][2][col]) + shl[u][3][col];
-            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-            _Float16 *orow = lds + (16 * (4 * NOWN + u) + col) * QS::QSTR + 4 * grp;
-#pragma unroll
-            for (int j = 0; j < NDQ; ++j)
-                *(h4 *)(orow + 16 * (NDQ * q + j)) = __builtin_convertvector(osh[u][j] * inv, h4);
-            const int tile = tm.t0 + 4 * NOWN + u;
-            const int r = 16 * tile + col;
-            const bool writer = tile < tm.t_end && r < a.M && grp == 0 && q == 0;
-            const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(msh[u], lt)), rwm,
-                                                  writer ? rowi * 4u : kOffNone, 0, 0);
-        }
-    }
-    __syncthreads();  // E3: every row is in LDS
-    // contiguous 16-byte stores of the normalised rows (a 1 KB span per wave
-    // instruction) through a buffer over this split's block of the
-    // workspace; rows past the group's last drop out
-    {
-        const __amdgpu_buffer_rsrc_t rwo = raw_rsrc(a.ws_o + (int64_t)split * a.NR * D, (u32)a.NR * (u32)(2 * D));
-        const int nrows = min(16 * tm.t_end, a.M) - 16 * tm.t0;
-        const int r0 = tid / QS::PR;
-        RowWalk rw(a, gkv, 16 * tm.t0 + r0, QS::RS, 2 * D);
-        const u32 part = 16u * (u32)(tid % QS::PR);
-        const _Float16 *src = lds + r0 * QS::QSTR + 8 * (tid % QS::PR);
-#pragma unroll
-        for (int jj = 0; jj < QS::NQ; ++jj) {
-            const u4v v = *(const u4v *)(src + jj * QS::RS * QS::QSTR);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nrows ? rw.off + part : kOffNone, 0,
-                                                   0);
-            rw.next();
-        }
-    }
+    const SplitPtrs p = {a.k_cache, a.v_cache, a.q, a.ws_o, a.ws_m};
+    uint32_t next = 0;
+    ws_split<NOWN, NSH>(a, p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, nullptr, next);
 }
 
 split_fn pick_split_q4ws(int D, int nown, int nsh)
