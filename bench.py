@@ -57,7 +57,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_128k_q4_0_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_128k_q4_0_hbm_traffic.md")
 
 
 def kernel_sources_sha256():
@@ -76,9 +76,9 @@ def kernel_sources_sha256():
 
 
 def measured_traffic():
-    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE and
-    WRITE_SIZE passes (copy-calibrated) stored under profiles/, or None when
-    the kernels have changed since they were taken."""
+    """HBM bytes per step launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE
+    passes (copy-calibrated) stored under profiles/, or None when the kernels
+    have changed since they were taken."""
     try:
         fields = {}
         with open(TRAFFIC_PROFILE) as f:
@@ -427,9 +427,17 @@ def main():
     def accept():
         tv.tree_accept(lg, parent, tokens, am, res, aws, stream)
 
-    def step(i):
+    def step_separate(i):
         attn(i)
         accept()
+
+    # the step: one launch of the work-queue kernel (tree_verify_step over
+    # the one layer; its split, merge and acceptance items)
+    sws = torch.zeros(tv.tv_step_workspace_bytes(desc, 1, vocab), dtype=torch.uint8, device=dev)
+    step_arrs = [tv.step_layers([(kc, vc, q, kt, vt, out)]) for kc, vc in caches]
+
+    def step(i):
+        tv.tree_verify_step(desc, step_arrs[i % n_copies], lg, tokens, am, res, sws, stream)
 
     R = T
     kv_bytes = 2 * Hkv * R * (D // 32 * 18)
@@ -468,19 +476,34 @@ def main():
         cfg["full_step_32k_16_layers"] = fs
         extra["configs"] = cfg
 
-    # ---- headline: W warm-up steps, then exactly K timed steps
+    # ---- headline: W warm-up steps, then exactly K timed steps. Before
+    # them, 200 steps that settle the device after the per-workload records
+    # (which allocate and free gigabytes: a short bracket right after that ran
+    # 10-20% slow).
+    if not args.no_configs:
+        for i in range(200):
+            step(i)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    res.fill_(-1)
     ms_step = timed(torch, stream, step, args.steps)
-    # the two parts of a step on their own (same stream, same rotation)
+    assert int(res[0].item()) == planted_L
+    # the step kernel's duration for the roofline (median of six parts), and
+    # the same step as separate launches (attention, then acceptance)
+    ms_kernel = timed_median(torch, stream, step, max(args.steps, 300))
+    timed(torch, stream, step_separate, 50)
+    ms_sep = timed_median(torch, stream, step_separate, max(args.steps, 300))
     ms_attn = timed_median(torch, stream, attn, max(args.steps, 300))
     ms_accept = timed_median(torch, stream, lambda i: accept(), max(args.steps, 300))
     assert int(res[0].item()) == planted_L
-    log(f"headline: {ms_step * 1e3:.1f} us per step, attention {ms_attn * 1e3:.1f} us")
+    log(f"headline: {ms_step * 1e3:.1f} us per step (one launch; {ms_kernel * 1e3:.1f} us median), "
+        f"separate launches {ms_sep * 1e3:.1f} us, attention {ms_attn * 1e3:.1f} us")
 
-    kv_gbps = kv_bytes / (ms_attn * 1e-3) / 1e9
-    tflops = flops / (ms_attn * 1e-3) / 1e12
+    kv_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
+    kv_gbps_attn = kv_bytes / (ms_attn * 1e-3) / 1e9
+    tflops = flops / (ms_kernel * 1e-3) / 1e12
+    tflops_attn = flops / (ms_attn * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_step,
@@ -497,22 +520,28 @@ def main():
         "config": {
             "workload": (f"one verify step: tree-verify attention (1 layer, {Hq} q / {Hkv} kv heads, head_dim {D}, "
                          f"ctx {T}, no window, Q4_0 KV, budget-22 tree of {n} nodes) + greedy acceptance "
-                         f"over {n}x{vocab} fp32 logits"),
+                         f"over {n}x{vocab} fp32 logits, as one launch (tree_verify_step)"),
             "kv": "q4_0", "n_ctx": T, "window": 0, "n_nodes": n, "vocab": vocab, "kv_copies_rotated": n_copies,
         },
         "kv_gbps": kv_gbps,
         "kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
-        "attn_us": ms_attn * 1e3,
-        "accept_us": ms_accept * 1e3,
+        "step_plan": tv.tv_step_plan(desc, 1, vocab),
+        "separate_launches": {
+            "ms_per_step": ms_sep, "attn_us": ms_attn * 1e3, "accept_us": ms_accept * 1e3,
+            "kv_gbps_attention": kv_gbps_attn, "tflops_attention": tflops_attn,
+            "frac_mfma_attention": tflops_attn / MFMA_FP16_PEAK_TFLOPS,
+            "note": "tree_verify_attn (split + merge kernels) then tree_accept, medians of six parts",
+        },
         "roofline": {
-            "kernel": "tree_verify_attn launch (split kernel + merge kernel)",
+            "kernel": "step_kernel<2, 1> (tree_verify_step: split, merge and acceptance items of the step)",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MFMA_FP16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
+            "kernel_us": ms_kernel * 1e3,
             "traffic": measured_traffic(),
-            "traffic_unit": "bytes per attention launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
+            "traffic_unit": "bytes per step launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
             "algorithmic_flops": flops,
             "algorithmic_kv_bytes": kv_bytes,
         },

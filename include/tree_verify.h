@@ -343,7 +343,9 @@ TV_API size_t tv_step_workspace_bytes(const tv_attn_desc *d, int32_t n_layers, i
 typedef struct tv_step_plan_info {
     int32_t launches;   /* kernel launches per call: 1 with the work-queue kernel */
     int32_t workgroups; /* workgroups of the work-queue kernel, 0 without it */
-    int64_t items;      /* its work items: acceptance, split and merge items */
+    int32_t splits;     /* key-range splits per KV head and row group of every layer */
+    int32_t row_groups;
+    int64_t items;      /* work items: acceptance, split and merge items */
     uint64_t workspace_bytes;
 } tv_step_plan_info;
 
@@ -353,10 +355,15 @@ TV_API int tv_step_plan(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, 
 
 /*
  * One verify step over n_layers attention layers and the acceptance,
- * asynchronous on `stream`. Results equal, bit for bit, those of
- * tree_verify_attn(d, &layers[l], ...) for l = 0 .. n_layers-1 followed by
- * tree_accept(logits, d->n_nodes, vocab, d->parent, tokens, argmax_out,
- * result_out, ...), with the same checks and error codes.
+ * asynchronous on `stream`: the results of tree_verify_attn(d, &layers[l],
+ * ...) for l = 0 .. n_layers-1 followed by tree_accept(logits, d->n_nodes,
+ * vocab, d->parent, tokens, argmax_out, result_out, ...), with the same
+ * checks, error codes and accuracy. The acceptance is bit for bit the same;
+ * the attention is too where the step splits the keys as tree_verify_attn
+ * does (tv_step_plan's splits equal tv_attn_plan's: one layer, long
+ * contexts), and otherwise differs only by the rounding of the per-split
+ * partial states (several layers share the device, so each layer's keys are
+ * cut into fewer, longer splits).
  *
  * d           one descriptor for every layer (tree, heads, head_dim, context,
  *             window, scale, cache type and strides).

@@ -3,10 +3,12 @@ plus the acceptance) in one launch of the work-queue kernel, or as the same
 separate launches where the plan has no work-queue kernel.
 
 The step's outputs must equal, bit for bit, those of tree_verify_attn per
-layer followed by tree_accept (the same split and merge arithmetic), and the
-acceptance must equal the oracle's; the attention of some layers is also
-checked against the oracle directly. Repeated calls on one workspace check
-that the queue counters are left zero.
+layer followed by tree_accept (the same split and merge arithmetic) where
+the step splits the keys as tree_verify_attn does (one layer); with several
+layers it takes fewer splits per layer, and every layer is then compared
+with the separate calls within the attention bound and some against the
+oracle. The acceptance must equal the oracle's. Repeated calls on one
+workspace check that the queue counters are left zero.
 """
 
 import numpy as np
@@ -85,14 +87,20 @@ def check_step(inps, vocab, seed, expect_launches=None, oracle_layers=()):
     ram, rres = oracle.accept(logits_np, parent, tokens)
     assert np.array_equal(ref[1], ram) and np.array_equal(ref[2], rres)
     assert int(rres[0]) == L
+    same_splits = plan["splits"] == tv.tv_attn_plan(desc)["splits"]
     for rep in range(2):
         got = run_step(tv, torch, desc, tens, inps[0], logits, tokens, ws)
         for l, (g, r) in enumerate(zip(got[0], ref[0])):
-            assert np.array_equal(g, r), ("layer", l, "call", rep, np.nanmax(np.abs(g - r)))
+            if same_splits:
+                assert np.array_equal(g, r), ("layer", l, "call", rep, np.nanmax(np.abs(g - r)))
+            else:
+                assert rownorm_err(g.astype(np.float64), r.astype(np.float64)) <= TOL, ("layer", l, "call", rep)
         assert np.array_equal(got[1], ram) and np.array_equal(got[2], rres), rep
         assert header_clear(ws), rep
     for l in oracle_layers:
-        err = rownorm_err(ref[0][l].astype(np.float64), oracle.attn(inps[l]))
+        want = oracle.attn(inps[l])
+        assert rownorm_err(ref[0][l].astype(np.float64), want) <= TOL, l
+        err = rownorm_err(got[0][l].astype(np.float64), want)
         assert err <= TOL, (l, err)
     return plan
 
@@ -136,16 +144,16 @@ def test_step_equals_separate_calls(shape):
     inps = _same_tree([synth.attn_inputs(**dict(w, seed=9100 + 7 * l + T)) for l in range(L)])
     for x in inps:
         x["window"] = W
-    plan = check_step(inps, vocab, 9200 + T, expect_launches=1 if single else None, oracle_layers=(L - 1,))
+    plan = check_step(inps, vocab, 9200 + T, expect_launches=1 if single else None, oracle_layers=range(L))
     if single is False:
         assert plan["launches"] > 1 and plan["workgroups"] == 0
 
 
 def test_full_step_16_layers_one_launch():
     """The 16-layer verify step at 32768 rows (trees 0 and 1 of its 64 on one
-    workspace): one launch, equal to the separate calls bit for bit, the
-    planted acceptance exact, and layer 15 of tree 1 against the oracle on
-    every row."""
+    workspace): one launch, every layer within the attention bound of the
+    separate calls, the planted acceptance exact, and layer 15 of tree 1
+    against the oracle on every row."""
     import torch
 
     import tree_verify_attention_ddtree_amd as tv
@@ -164,8 +172,9 @@ def test_full_step_16_layers_one_launch():
         logits = torch.from_numpy(t["logits"]).cuda()
         got = run_step(tv, torch, desc, tens, inps[0], logits, t["tokens"], ws)
         ref = run_separate(tv, torch, desc, tens, inps[0], logits, t["tokens"])
+        assert plan["splits"] == 32  # half the single-layer count: items of 16 chunks
         for l in range(16):
-            assert np.array_equal(got[0][l], ref[0][l]), (tree, l)
+            assert rownorm_err(got[0][l].astype(np.float64), ref[0][l].astype(np.float64)) <= TOL, (tree, l)
         ram, rres = oracle.accept(t["logits"], t["parent"], t["tokens"])
         assert np.array_equal(got[1], ram) and np.array_equal(got[2], rres)
         assert int(got[2][0]) == t["n_acc"]

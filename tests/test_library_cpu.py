@@ -295,14 +295,25 @@ def test_step_plan():
         d, keep = tv.make_desc(parent, 24, 4, D, kv, n_ctx, window, 0.0625, row, row * max(n_ctx, 1))
         return tv.tv_step_plan(d, L, vocab, 256), tv.tv_attn_plan(d, 256)
 
+    # one layer: the split count of tree_verify_attn
+    p, a = plan(Q, 131072, 1, 152000)
+    assert a["kernel"] == tv.TV_SPLIT_Q4_0_WS and a["splits"] == 64 and p["splits"] == 64
+    assert p["items"] == (23 * 19 + 1) // 2 + 64 * 4 + (23 * 24 + 3) // 4
+    assert p["workspace_bytes"] == 2048 + (a["workspace_bytes"] + 255) // 256 * 256
+    # 16 layers at 32K: half the splits (at most 16 chunks per split item)
     p, a = plan(Q, 32768, 16, 152000)
-    assert a["kernel"] == tv.TV_SPLIT_Q4_0_WS and a["splits"] == 64
-    n_items = (23 * 19 + 1) // 2 + 16 * 64 * 4 + 15 * ((23 * 24 + 7) // 8) + (23 * 24 + 3) // 4
+    assert a["splits"] == 64 and (p["splits"], p["row_groups"]) == (32, 1)
+    n_items = (23 * 19 + 1) // 2 + 16 * 32 * 4 + 15 * ((23 * 24 + 7) // 8) + (23 * 24 + 3) // 4
     assert (p["launches"], p["workgroups"], p["items"]) == (1, n_items, n_items)
-    assert p["workspace_bytes"] == 2048 + 16 * ((a["workspace_bytes"] + 255) // 256 * 256)
+    layer = 32 * 23 * 24 * (2 * 256 + 4)
+    assert p["workspace_bytes"] == 2048 + 16 * ((layer + 255) // 256 * 256)
+    # 16 layers at 8K: at least two rounds of split items over 256 CUs
+    p, a = plan(Q, 8192, 16, 152000)
+    assert (a["splits"], p["splits"]) == (64, 8)
     # a 2048-row window: two row groups per KV head
     p, a = plan(Q, 61440, 3, 1000, window=2048)
-    assert a["row_groups"] == 2 and p["items"] == (23 + 1) // 2 + 3 * 32 * 4 * 2 + 2 * 69 + 138
+    assert a["row_groups"] == 2 and (p["splits"], p["row_groups"]) == (32, 2)
+    assert p["items"] == (23 + 1) // 2 + 3 * 32 * 4 * 2 + 2 * 69 + 138
     # separate launches: F16, head_dim 128, no whole chunk, a masked plan
     for kv, n_ctx, D in ((F, 32768, 256), (Q, 32768, 128), (Q, 50, 256), (Q, 4096 + 37, 256)):
         p, a = plan(kv, n_ctx, 4, 1000, D=D)

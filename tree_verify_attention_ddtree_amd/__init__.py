@@ -79,6 +79,8 @@ class TvStepPlanInfo(ctypes.Structure):
     _fields_ = [
         ("launches", ctypes.c_int32),
         ("workgroups", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("row_groups", ctypes.c_int32),
         ("items", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
     ]

@@ -16,15 +16,18 @@
 // ticket order whatever order the hardware dispatches workgroups in.
 // (A persistent loop over items would keep per-thread values live across the
 // split body, whose math waves use every register.) Items in ticket order:
-//   S_0, S_1                the split items of layers 0 and 1 (split, KV
-//                           head, row group): the warp-specialised split
+//   S_0 .. S_{g-1}          the split items of the first g layers (split,
+//                           KV head, row group): the warp-specialised split
 //                           body of tv_split_q4ws.h;
-//   S_k, M_{k-2}            for k = 2 .. L-1: layer k's split items, then
-//                           the merge items of layer k - 2 (8 output rows
-//                           each, two at a time, one per half workgroup),
-//                           whose splits finished a layer earlier;
-//   M_{L-2}, A, M_{L-1}     the last merges (4 rows per item for the last
-//                           layer) around the acceptance items (one
+//   S_k, M_{k-g}            for k = g .. L-1: layer k's split items, then the
+//                           merge items of layer k - g (8 output rows each,
+//                           two at a time, one per half workgroup); the lag g
+//                           puts about one round of split items (one per
+//                           compute unit) between a layer's splits and its
+//                           merges, so the merges rarely wait;
+//   M_{L-g} .. M_{L-2}, A, M_{L-1}
+//                           the remaining merges (4 rows per item for the
+//                           last layer) around the acceptance items (one
 //                           8192-logit slice per half workgroup), so that
 //                           the workgroups freed by the last splits have
 //                           work while the slowest of them finish.
@@ -94,6 +97,7 @@ struct StepArgs {
     int32_t n_merge;   // merge items per layer (kMergeRowsMid rows each)
     int32_t n_merge_last;  // merge items of the last layer (kMergeRowsLast rows each)
     int32_t H_kv;
+    int32_t lag;  // layers between a layer's split items and its merge items
     int32_t total;
 };
 static_assert(sizeof(StepArgs) <= 4096, "kernel arguments of the step kernel");
@@ -108,22 +112,21 @@ struct Item {
 
 __device__ __forceinline__ Item decode(const StepArgs &s, int t)
 {
-    const int L = s.n_layers, S = s.n_split, M = s.n_merge;
+    const int L = s.n_layers, S = s.n_split, M = s.n_merge, lag = s.lag;
     int u = t;
-    const int head = (L < 2 ? L : 2) * S;  // S_0, S_1
-    if (u < head) return {1, u / S, u % S, 0};
-    u -= head;
+    const int nh = L < lag ? L : lag;  // blocks S_k alone, k < lag
+    if (u < nh * S) return {1, u / S, u % S, 0};
+    u -= nh * S;
     const int blk = S + M;
-    const int nmid = L > 2 ? L - 2 : 0;  // blocks S_k, M_{k-2} for k = 2 .. L-1
-    if (u < nmid * blk) {
-        const int k = 2 + u / blk, r = u % blk;
-        return r < S ? Item{1, k, r, 0} : Item{2, k - 2, r - S, kMergeRowsMid};
+    const int nb = L - nh;  // blocks S_k, M_{k-lag} for k = lag .. L-1
+    if (u < nb * blk) {
+        const int k = lag + u / blk, r = u % blk;
+        return r < S ? Item{1, k, r, 0} : Item{2, k - lag, r - S, kMergeRowsMid};
     }
-    u -= nmid * blk;
-    if (L >= 2) {
-        if (u < M) return {2, L - 2, u, kMergeRowsMid};
-        u -= M;
-    }
+    u -= nb * blk;
+    const int nt = L - 1 - nb;  // merges of layers nb .. L-2 after every split
+    if (u < nt * M) return {2, nb + u / M, u % M, kMergeRowsMid};
+    u -= nt * M;
     if (u < s.n_accept) return {0, 0, u, 0};
     return {2, L - 1, u - s.n_accept, kMergeRowsLast};
 }
@@ -215,6 +218,15 @@ static const void *pick_step(int nown, int nsh)
     return nullptr;
 }
 
+// A layer's merge items are queued behind about one round of later split
+// items (one per compute unit), so that its own splits have finished when
+// they start: ceil(n_cu / split items per layer) + 1 layers, at least 2.
+static int step_lag(int n_cu, int n_split)
+{
+    const int l = (n_cu + n_split - 1) / n_split + 1;
+    return l < 2 ? 2 : l;
+}
+
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t step_layer_bytes(const tv_attn_desc *d, const SplitPlan &p) { return round256(attn_ws_bytes(d, p)); }
@@ -297,6 +309,7 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
     s.n_merge_last = (NR + kMergeRowsLast - 1) / kMergeRowsLast;
     s.n_accept = (s.ac.n * s.ac.n_slices + 1) / 2;
     s.H_kv = d->n_kv_heads;
+    s.lag = step_lag(n_cu, s.n_split);
     s.total = (int32_t)items;
     const void *fn = pick_step(plan.rows.nown, plan.rows.nsh);
     void *args[] = {(void *)&s};
