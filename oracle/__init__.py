@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tvref.c")
-_LIB = os.path.join(_HERE, "libtvref.so")
+# TVREF_LIB names another build of tvref.c to load instead (the sanitizer
+# run of tests/sanitize/run_cpu_suite.sh); it is loaded as it is
+_LIB = os.environ.get("TVREF_LIB") or os.path.join(_HERE, "libtvref.so")
 
 KV_F16 = 0
 KV_Q4_0 = 1
@@ -41,7 +43,8 @@ def build() -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.environ.get("TVREF_LIB") and (not os.path.exists(_LIB) or
+                                                os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p

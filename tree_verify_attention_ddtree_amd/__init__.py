@@ -93,16 +93,20 @@ class TvError(RuntimeError):
 
 
 def lib_path() -> str:
-    return _build.LIB
+    """libtv.so next to this file, or the build TV_LIB names (the host-only
+    sanitizer build of tests/sanitize/run_cpu_suite.sh, whose launches all
+    fail with TV_E_HIP)."""
+    return os.environ.get("TV_LIB") or _build.LIB
 
 
 def lib():
     """The loaded libtv.so; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            raise RuntimeError(f"{_build.LIB} is missing: build it first (python -m tree_verify_attention_ddtree_amd.build)")
-        L = ctypes.CDLL(_build.LIB)
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first (python -m tree_verify_attention_ddtree_amd.build)")
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L.tv_strerror.argtypes = [ctypes.c_int]
         L.tv_strerror.restype = ctypes.c_char_p

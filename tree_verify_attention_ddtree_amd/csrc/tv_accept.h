@@ -13,7 +13,6 @@
 namespace tv {
 
 constexpr int kAccThreads = 256;
-constexpr int kSliceFloats = 8192;  // logits per workgroup of kernel 1
 
 // Integer tests only, so that the order holds whatever floating-point
 // options the including file is compiled with.
@@ -50,7 +49,7 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t v)
 constexpr size_t kRowsDoneOff = 0;
 constexpr size_t kRowCountOff = 64;
 constexpr size_t kRowKeyOff = kRowCountOff + 4 * TV_MAX_NODES;
-constexpr size_t kAcceptWsBytes = kRowKeyOff + 8 * TV_MAX_NODES;
+static_assert(kRowKeyOff + 8 * TV_MAX_NODES == kAcceptWsBytes, "acceptance state layout");
 
 struct AcceptArgs {
     const float *logits;

@@ -32,8 +32,6 @@ __global__ void __launch_bounds__(kAccThreads) accept_kernel(const AcceptArgs a)
 
 static int64_t n_slices_for(int vocab) { return ((int64_t)vocab + kSliceFloats - 1) / kSliceFloats; }
 
-size_t accept_ws_bytes(int, int) { return kAcceptWsBytes; }
-
 void fill_accept_args(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                       int32_t *argmax_out, int32_t *result_out, uint8_t *ws, AcceptArgs *out)
 {

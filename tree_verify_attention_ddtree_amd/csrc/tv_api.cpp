@@ -13,16 +13,12 @@ namespace tv {
 
 int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
                 hipStream_t stream);
-size_t accept_ws_bytes(int n, int vocab);
 int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
 int launch_accept_noalloc(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                           int32_t *argmax_out, int32_t *result_out, hipStream_t stream);
 int launch_stream_probe(const void *buf, uint64_t bytes, int kind, uint32_t *checksums, int n_wg,
                         hipStream_t stream);
-size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers);
-void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int n_cu, int *launches,
-                int *workgroups, int64_t *items);
 int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers, const float *logits, int vocab,
                 const int32_t *tokens, int32_t *argmax_out, int32_t *result_out, void *ws, int n_cu,
                 const SplitPlan &plan, hipStream_t stream);
@@ -190,6 +186,57 @@ size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p)
     return (size_t)p.S * NR * ((size_t)d->head_dim * 2 + sizeof(float));
 }
 
+int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p)
+{
+    if (p.S == 0) return TV_SPLIT_NONE;
+    if (d->kv_type == TV_KV_Q4_0 && !p.mask && ws_layout(d->head_dim, p.rows.nown, p.rows.nsh))
+        return TV_SPLIT_Q4_0_WS;
+    return d->kv_type == TV_KV_Q4_0 ? TV_SPLIT_Q4_0 : TV_SPLIT_F16;
+}
+
+// A layer's merge items are queued behind about one round of later split
+// items (one per compute unit), so that its own splits have finished when
+// they start: ceil(n_cu / split items per layer) + 1 layers, at least 2.
+int step_lag(int n_cu, int n_split)
+{
+    const int l = (n_cu + n_split - 1) / n_split + 1;
+    return l < 2 ? 2 : l;
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t step_layer_bytes(const tv_attn_desc *d, const SplitPlan &p) { return round256(attn_ws_bytes(d, p)); }
+
+size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers)
+{
+    return kStepHeader + (size_t)n_layers * step_layer_bytes(d, p);
+}
+
+// Launches of one step call (1 with the work-queue kernel) and its work
+// items (one workgroup each); 0 workgroups when the plan has no work-queue
+// kernel (then the step makes the separate launches).
+void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
+                int64_t *items)
+{
+    // (the merge items address a layer's partials with 31-bit offsets)
+    const bool fits = (int64_t)p.S * d->n_nodes * d->n_q_heads * (2 * d->head_dim) < ((int64_t)1 << 31);
+    const int64_t NR = (int64_t)d->n_nodes * d->n_q_heads;
+    const int64_t n_split = (int64_t)p.S * d->n_kv_heads * p.rows.groups;
+    const int64_t n_merge = (NR + kMergeRowsMid - 1) / kMergeRowsMid;
+    const int64_t n_last = (NR + kMergeRowsLast - 1) / kMergeRowsLast;
+    const int64_t slices = (int64_t)d->n_nodes * (((int64_t)vocab + kSliceFloats - 1) / kSliceFloats);
+    const int64_t total = (slices + 1) / 2 + n_layers * n_split + (n_layers - 1) * n_merge + n_last;
+    if (split_kernel_kind(d, p) == TV_SPLIT_Q4_0_WS && fits && total <= INT32_MAX) {
+        *items = total;
+        *workgroups = (int)total;
+        *launches = 1;
+    } else {
+        *items = 0;
+        *workgroups = 0;
+        *launches = n_layers * (p.S > 0 ? 2 : 1) + 1;
+    }
+}
+
 int device_cu_count(int *n_cu)
 {
     // cached per device; the count of a device never changes
@@ -299,7 +346,7 @@ int tree_verify_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, void *workspa
 size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab)
 {
     if (n_nodes < 1 || n_nodes > TV_MAX_NODES || vocab < 1) return 0;
-    return tv::accept_ws_bytes(n_nodes, vocab);
+    return tv::kAcceptWsBytes;
 }
 
 static int check_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32_t *parent,
@@ -318,7 +365,7 @@ int tree_accept(const float *logits, int32_t n_nodes, int32_t vocab, const int32
 {
     int rc = check_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out);
     if (rc) return rc;
-    const size_t need = tv::accept_ws_bytes(n_nodes, vocab);
+    const size_t need = tv::kAcceptWsBytes;
     if (!workspace || workspace_bytes < need) return TV_E_WORKSPACE;
     if (!aligned(workspace, 8)) return TV_E_ALIGN;
     return tv::launch_accept(logits, n_nodes, vocab, parent, tokens, argmax_out, result_out, workspace,
@@ -383,7 +430,7 @@ int tv_step_plan(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, int32_t
     memset(out, 0, sizeof(*out));
     int launches = 0, wgs = 0;
     int64_t items = 0;
-    tv::step_shape(d, plan, n_layers, vocab, cu, &launches, &wgs, &items);
+    tv::step_shape(d, plan, n_layers, vocab, &launches, &wgs, &items);
     out->launches = launches;
     out->workgroups = wgs;
     out->splits = plan.S;

@@ -466,15 +466,8 @@ static split_fn pick_split(int D, int kv, int nown, int nsh, bool mask)
 // has (head_dim 256; one or two own tiles per wave, at most two shared).
 split_fn pick_ws(const tv_attn_desc *d, const SplitPlan &p)
 {
-    if (d->kv_type != TV_KV_Q4_0 || p.mask) return nullptr;
+    if (d->kv_type != TV_KV_Q4_0 || p.mask || !ws_layout(d->head_dim, p.rows.nown, p.rows.nsh)) return nullptr;
     return pick_split_q4ws(d->head_dim, p.rows.nown, p.rows.nsh);
-}
-
-int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p)
-{
-    if (p.S == 0) return TV_SPLIT_NONE;
-    if (pick_ws(d, p)) return TV_SPLIT_Q4_0_WS;
-    return d->kv_type == TV_KV_Q4_0 ? TV_SPLIT_Q4_0 : TV_SPLIT_F16;
 }
 
 void fill_split_args(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, SplitArgs *out)

@@ -54,10 +54,33 @@ struct SplitPlan {
     int S;            // key-range splits per (KV head, row group)
 };
 
+// Tile layouts (own tiles per wave, shared tiles per workgroup) for which the
+// warp-specialised Q4_0 split kernel and the work-queue step kernel are
+// built (head_dim 256): the kernels' dispatch tables and the host planner
+// both read this.
+inline bool ws_layout(int D, int nown, int nsh)
+{
+    return D == 256 && ((nown == 1 && nsh >= 0 && nsh <= 2) || (nown == 2 && nsh >= 0 && nsh <= 1));
+}
+
+// Sizes the host side needs from the kernels' layouts.
+constexpr size_t kAcceptWsBytes = 832;  // acceptance state: counters, per-row maxima
+constexpr int kSliceFloats = 8192;      // logits per acceptance workgroup (slice)
+constexpr size_t kStepHeader = 2048;    // work-queue header of the step workspace
+constexpr int kMergeRowsMid = 8;        // output rows per step merge item (all but the last layer)
+constexpr int kMergeRowsLast = 4;       // ... of the last layer
+
 int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out);
 // Which split kernel a plan launches (TV_SPLIT_* of tree_verify.h).
 int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p);
 size_t attn_ws_bytes(const tv_attn_desc *d, const SplitPlan &p);
 int device_cu_count(int *n_cu);
+// The step's plan: its workspace, launches and work items, and the lag of
+// its merge items (see tv_step.hip).
+size_t step_layer_bytes(const tv_attn_desc *d, const SplitPlan &p);
+size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers);
+void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
+                int64_t *items);
+int step_lag(int n_cu, int n_split);
 
 }  // namespace tv

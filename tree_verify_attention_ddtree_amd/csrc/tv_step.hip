@@ -64,18 +64,16 @@ constexpr size_t kQExited = 4;      // u32 workgroups that left the loop
 constexpr size_t kQStatus = 8;      // u32 1 if a merge wait ran out
 constexpr size_t kQDone = 64;       // u32[TV_MAX_LAYERS] split items done per layer
 constexpr size_t kQAccept = 1024;   // acceptance state (kAcceptWsBytes)
-constexpr size_t kStepHeader = 2048;
 static_assert(kQDone + 4 * TV_MAX_LAYERS <= kQAccept && kQAccept + kAcceptWsBytes <= kStepHeader,
               "work-queue header layout");
 
-// Output rows per merge item (two at a time, one per half workgroup). A
-// merge row takes about 4 us at one workgroup per compute unit (latency
-// bound), and every item pays about 2 us of dispatch and ticket: merges that
-// run beside later layers' splits take 8 rows, the last layer's merges,
-// which end the step, 4 (16 layers at 32K rows: 533 us with 8 rows, 585 with
-// 4, 691 with 2; one layer at 128K rows: 111, 107 and 114 us).
-constexpr int kMergeRowsMid = 8;
-constexpr int kMergeRowsLast = 4;
+// Output rows per merge item (kMergeRowsMid, kMergeRowsLast), two at a time,
+// one per half workgroup. A merge row takes about 4 us at one workgroup per
+// compute unit (latency bound), and every item pays about 2 us of dispatch
+// and ticket: merges that run beside later layers' splits take 8 rows, the
+// last layer's merges, which end the step, 4 (16 layers at 32K rows: 533 us
+// with 8 rows, 585 with 4, 691 with 2; one layer at 128K rows: 111, 107 and
+// 114 us).
 
 struct StepLayer {
     SplitPtrs sp;
@@ -209,6 +207,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) step_kernel(const StepArgs s)
     }
 }
 
+// step kernel of a tile layout (every layout ws_layout accepts)
 static const void *pick_step(int nown, int nsh)
 {
 #define TV_CASE(O, S) \
@@ -216,48 +215,6 @@ static const void *pick_step(int nown, int nsh)
     TV_CASE(1, 0) TV_CASE(1, 1) TV_CASE(1, 2) TV_CASE(2, 0) TV_CASE(2, 1)
 #undef TV_CASE
     return nullptr;
-}
-
-// A layer's merge items are queued behind about one round of later split
-// items (one per compute unit), so that its own splits have finished when
-// they start: ceil(n_cu / split items per layer) + 1 layers, at least 2.
-static int step_lag(int n_cu, int n_split)
-{
-    const int l = (n_cu + n_split - 1) / n_split + 1;
-    return l < 2 ? 2 : l;
-}
-
-static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t step_layer_bytes(const tv_attn_desc *d, const SplitPlan &p) { return round256(attn_ws_bytes(d, p)); }
-
-size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers)
-{
-    return kStepHeader + (size_t)n_layers * step_layer_bytes(d, p);
-}
-
-// Launches of one step call (1 with the work-queue kernel) and its work
-// items (one workgroup each); 0 workgroups when the plan has no work-queue
-// kernel.
-void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int n_cu, int *launches,
-                int *workgroups, int64_t *items)
-{
-    // (the merge items address a layer's partials with 31-bit offsets)
-    const bool fits = (int64_t)p.S * d->n_nodes * d->n_q_heads * (2 * d->head_dim) < ((int64_t)1 << 31);
-    if (p.S > 0 && fits && pick_ws(d, p) && pick_step(p.rows.nown, p.rows.nsh)) {
-        const int64_t n_split = (int64_t)p.S * d->n_kv_heads * p.rows.groups;
-        const int64_t NR = (int64_t)d->n_nodes * d->n_q_heads;
-        const int64_t n_merge = (NR + kMergeRowsMid - 1) / kMergeRowsMid;
-        const int64_t n_last = (NR + kMergeRowsLast - 1) / kMergeRowsLast;
-        const int64_t slices = (int64_t)d->n_nodes * ((vocab + 8191) / 8192);
-        *items = (slices + 1) / 2 + n_layers * n_split + (n_layers - 1) * n_merge + n_last;
-        *workgroups = *items > INT32_MAX ? 0 : (int)*items;
-        *launches = 1;
-    } else {
-        *items = 0;
-        *workgroups = 0;
-        *launches = n_layers * (p.S > 0 ? 2 : 1) + 1;
-    }
 }
 
 int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, hipStream_t stream);
@@ -274,7 +231,7 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
     const size_t lb = step_layer_bytes(d, plan);
     int launches = 0, wgs = 0;
     int64_t items = 0;
-    step_shape(d, plan, n_layers, vocab, n_cu, &launches, &wgs, &items);
+    step_shape(d, plan, n_layers, vocab, &launches, &wgs, &items);
     if (wgs == 0) {
         // per-layer launches, then the acceptance, on the same stream
         for (int l = 0; l < n_layers; ++l) {
@@ -312,6 +269,7 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
     s.lag = step_lag(n_cu, s.n_split);
     s.total = (int32_t)items;
     const void *fn = pick_step(plan.rows.nown, plan.rows.nsh);
+    if (!fn) return TV_E_SHAPE;
     void *args[] = {(void *)&s};
     if (hipLaunchKernel(fn, dim3(wgs), dim3(kWsThreads), args, 0, stream) != hipSuccess) return TV_E_HIP;
     return TV_OK;
