@@ -57,7 +57,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "step_128k_q4_0_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_128k_q4_0_hbm_traffic.md")
 
 
 def kernel_sources_sha256():
@@ -76,9 +76,9 @@ def kernel_sources_sha256():
 
 
 def measured_traffic():
-    """HBM bytes per step launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE
-    passes (copy-calibrated) stored under profiles/, or None when the kernels
-    have changed since they were taken."""
+    """HBM bytes per attention launch (split and merge kernels) from the
+    rocprofv3 FETCH_SIZE and WRITE_SIZE passes (copy-calibrated) stored under
+    profiles/, or None when the kernels have changed since they were taken."""
     try:
         fields = {}
         with open(TRAFFIC_PROFILE) as f:
@@ -431,12 +431,16 @@ def main():
         attn(i)
         accept()
 
-    # the step: one launch of the work-queue kernel (tree_verify_step over
-    # the one layer; its split, merge and acceptance items)
+    # the step: the attention launch (split and merge kernels), then the
+    # acceptance launch. (The same step as one launch of the work-queue
+    # kernel, tree_verify_step, is timed beside it: 2-3% slower for one
+    # layer, where the split items fill the device once and the merges run as
+    # items of one workgroup per compute unit.)
+    step = step_separate
     sws = torch.zeros(tv.tv_step_workspace_bytes(desc, 1, vocab), dtype=torch.uint8, device=dev)
     step_arrs = [tv.step_layers([(kc, vc, q, kt, vt, out)]) for kc, vc in caches]
 
-    def step(i):
+    def step_one(i):
         tv.tree_verify_step(desc, step_arrs[i % n_copies], lg, tokens, am, res, sws, stream)
 
     R = T
@@ -489,21 +493,21 @@ def main():
     res.fill_(-1)
     ms_step = timed(torch, stream, step, args.steps)
     assert int(res[0].item()) == planted_L
-    # the step kernel's duration for the roofline (median of six parts), and
-    # the same step as separate launches (attention, then acceptance)
-    ms_kernel = timed_median(torch, stream, step, max(args.steps, 300))
-    timed(torch, stream, step_separate, 50)
-    ms_sep = timed_median(torch, stream, step_separate, max(args.steps, 300))
+    # the parts of a step on their own (medians of six runs of 50), and the
+    # one-launch form
     ms_attn = timed_median(torch, stream, attn, max(args.steps, 300))
     ms_accept = timed_median(torch, stream, lambda i: accept(), max(args.steps, 300))
+    ms_sep = timed_median(torch, stream, step, max(args.steps, 300))
+    res.fill_(-1)
+    timed(torch, stream, step_one, 50)
+    ms_one = timed_median(torch, stream, step_one, max(args.steps, 300))
     assert int(res[0].item()) == planted_L
-    log(f"headline: {ms_step * 1e3:.1f} us per step (one launch; {ms_kernel * 1e3:.1f} us median), "
-        f"separate launches {ms_sep * 1e3:.1f} us, attention {ms_attn * 1e3:.1f} us")
+    log(f"headline: {ms_step * 1e3:.1f} us per step ({ms_sep * 1e3:.1f} us median), attention {ms_attn * 1e3:.1f} us, "
+        f"one launch {ms_one * 1e3:.1f} us")
 
-    kv_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
-    kv_gbps_attn = kv_bytes / (ms_attn * 1e-3) / 1e9
-    tflops = flops / (ms_kernel * 1e-3) / 1e12
-    tflops_attn = flops / (ms_attn * 1e-3) / 1e12
+    kv_gbps = kv_bytes / (ms_attn * 1e-3) / 1e9
+    tflops = flops / (ms_attn * 1e-3) / 1e12
+    tflops_one = flops / (ms_one * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_step,
@@ -520,28 +524,29 @@ def main():
         "config": {
             "workload": (f"one verify step: tree-verify attention (1 layer, {Hq} q / {Hkv} kv heads, head_dim {D}, "
                          f"ctx {T}, no window, Q4_0 KV, budget-22 tree of {n} nodes) + greedy acceptance "
-                         f"over {n}x{vocab} fp32 logits, as one launch (tree_verify_step)"),
+                         f"over {n}x{vocab} fp32 logits"),
             "kv": "q4_0", "n_ctx": T, "window": 0, "n_nodes": n, "vocab": vocab, "kv_copies_rotated": n_copies,
         },
         "kv_gbps": kv_gbps,
         "kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
-        "step_plan": tv.tv_step_plan(desc, 1, vocab),
-        "separate_launches": {
-            "ms_per_step": ms_sep, "attn_us": ms_attn * 1e3, "accept_us": ms_accept * 1e3,
-            "kv_gbps_attention": kv_gbps_attn, "tflops_attention": tflops_attn,
-            "frac_mfma_attention": tflops_attn / MFMA_FP16_PEAK_TFLOPS,
-            "note": "tree_verify_attn (split + merge kernels) then tree_accept, medians of six parts",
+        "ms_per_step_median": ms_sep,
+        "attn_us": ms_attn * 1e3,
+        "accept_us": ms_accept * 1e3,
+        "one_launch_step": {
+            "ms_per_step": ms_one, "steps_per_s": 1e3 / ms_one, "tflops": tflops_one,
+            "frac_mfma": tflops_one / MFMA_FP16_PEAK_TFLOPS, "plan": tv.tv_step_plan(desc, 1, vocab),
+            "note": "tree_verify_step: split, merge and acceptance items of the step in one launch (median of six parts)",
         },
         "roofline": {
-            "kernel": "step_kernel<2, 1> (tree_verify_step: split, merge and acceptance items of the step)",
+            "kernel": "tree_verify_attn launch: split_q4ws_kernel<2, 1> + merge_kernel<256>",
             "bound": "mfma",
             "achieved": tflops,
             "peak": MFMA_FP16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_FP16_PEAK_TFLOPS,
-            "kernel_us": ms_kernel * 1e3,
+            "launch_us": ms_attn * 1e3,
             "traffic": measured_traffic(),
-            "traffic_unit": "bytes per step launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
+            "traffic_unit": "bytes per attention launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1, copy-calibrated)",
             "algorithmic_flops": flops,
             "algorithmic_kv_bytes": kv_bytes,
         },

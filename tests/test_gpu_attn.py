@@ -157,7 +157,7 @@ def test_tile_layouts(Hq, Hkv, n, D, kv):
                                       (10, {"q4_0": (1, 0), "f16": (1, 0)}), (11, {"q4_0": (1, 1), "f16": (1, 1)}),
                                       (16, {"q4_0": (1, 2), "f16": (1, 2)}), (26, {"q4_0": (1, 1), "f16": (1, 1)})])
 def test_tile_layouts_27b_heads(n, layout, kv):
-    """The 27B head layout (24 q / 4 kv heads) over 64 whole chunks per KV
+    """The 27B head layout (24 q / 4 kv heads) over 256 whole chunks per KV
     head: 8, 20, 30, 23, 10, 11 and 16 nodes make 3, 8, 12, 9, 4, 5 and 6
     query tiles in one row group; 26 nodes make 10 tiles, cut into two row
     groups of five (a group holds at most three tile slots per wave). The
@@ -166,11 +166,11 @@ def test_tile_layouts_27b_heads(n, layout, kv):
     (unmasked; every layout of the warp-specialised Q4_0 kernel is among
     them)."""
     import tree_verify_attention_ddtree_amd as tv
-    inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=4096, n_nodes=n, depth_cap=16,
+    inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=16384, n_nodes=n, depth_cap=16,
                             seed=3000 + n, kv=kv)
     kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
     row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
-    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, 4096, 0, inp["scale"], row, row * 4096)
+    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, 16384, 0, inp["scale"], row, row * 16384)
     plan = tv.tv_attn_plan(desc)
     assert (plan["own_tiles"], plan["shared_tiles"]) == layout[kv], plan
     assert plan["row_groups"] == (2 if n == 26 else 1) and plan["masked"] == 0, plan

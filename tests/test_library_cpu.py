@@ -208,24 +208,37 @@ def _plan(Hq, Hkv, n, D, kv, n_ctx, window=0, window_mode=0, n_cu=256):
 
 
 def test_plan_query_layouts():
-    """The 27B head layout (24 q / 4 kv heads) on 256 compute units, 64
+    """The 27B head layout (24 q / 4 kv heads) on 256 compute units, 256
     whole chunks per KV head: 8, 20 and 30 nodes give 3, 8 and 12 query
     tiles, which the Q4_0 kernels take as three shared tiles, two own tiles
     per wave and three own tiles per wave, with one row group."""
     Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
-    p = _plan(24, 4, 8, 256, Q, 4096)
+    p = _plan(24, 4, 8, 256, Q, 16384)
     assert (p["own_tiles"], p["shared_tiles"], p["row_groups"], p["masked"]) == (0, 3, 1, 0)
-    assert (p["splits"], p["chunks"], p["kernel"]) == (64, 64, tv.TV_SPLIT_Q4_0)
-    p = _plan(24, 4, 8, 256, F, 4096)
+    assert (p["splits"], p["chunks"], p["kernel"]) == (64, 256, tv.TV_SPLIT_Q4_0)
+    p = _plan(24, 4, 8, 256, F, 16384)
     assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16)
     for kv in (Q, F):
-        p = _plan(24, 4, 20, 256, kv, 4096)
+        p = _plan(24, 4, 20, 256, kv, 16384)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (2, 0, 1)
         assert p["kernel"] == (tv.TV_SPLIT_Q4_0_WS if kv == Q else tv.TV_SPLIT_F16)
-        p = _plan(24, 4, 30, 256, kv, 4096)
+        p = _plan(24, 4, 30, 256, kv, 16384)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (3, 0, 1)
         # three own tiles per wave do not fit two waves per SIMD
         assert p["kernel"] == (tv.TV_SPLIT_Q4_0 if kv == Q else tv.TV_SPLIT_F16)
+    # at most two chunks a split (8K and below): half the splits, two row
+    # groups (budget 22: groups of 5 and 4 tiles, one own tile per wave)
+    p = _plan(24, 4, 23, 256, Q, 8192)
+    assert (p["splits"], p["row_groups"], p["own_tiles"], p["shared_tiles"]) == (32, 2, 1, 1)
+    assert p["kernel"] == tv.TV_SPLIT_Q4_0_WS
+    p = _plan(24, 4, 23, 256, Q, 16384)
+    assert (p["splits"], p["row_groups"]) == (64, 1)
+    # not where a group would leave the warp-specialised layouts (10 nodes:
+    # groups of two shared tiles) nor for F16 caches
+    p = _plan(24, 4, 10, 256, Q, 8192)
+    assert (p["splits"], p["row_groups"], p["kernel"]) == (64, 1, tv.TV_SPLIT_Q4_0_WS)
+    p = _plan(24, 4, 23, 256, F, 8192)
+    assert (p["splits"], p["row_groups"]) == (64, 1)
     # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits,
     # on the warp-specialised kernel (head_dim 256)
     p = _plan(24, 4, 23, 256, Q, 131072)
@@ -309,7 +322,7 @@ def test_step_plan():
     assert p["workspace_bytes"] == 2048 + 16 * ((layer + 255) // 256 * 256)
     # 16 layers at 8K: at least two rounds of split items over 256 CUs
     p, a = plan(Q, 8192, 16, 152000)
-    assert (a["splits"], p["splits"]) == (64, 8)
+    assert (a["splits"], a["row_groups"], p["splits"], p["row_groups"]) == (32, 2, 8, 1)
     # a 2048-row window: two row groups per KV head
     p, a = plan(Q, 61440, 3, 1000, window=2048)
     assert a["row_groups"] == 2 and (p["splits"], p["row_groups"]) == (32, 2)
