@@ -233,6 +233,29 @@ struct Q4Loader {
 
     static constexpr int V_PIECES = Sh::NKV >= 2 ? 4 : 2;
 
+    // V piece p (NKV >= 2): code dword k = p >> 1 and element half (p & 1 ?
+    // the "b" bytes : the "a" bytes) of the NKV keys, dequantised; key pair
+    // pr of vals[pr][t] holds element e0 + {0, 1, 16, 17}[t] + 2 (p & 1) of
+    // block vb with e0 = 8 vh + 4 k (keys 2 pr and 2 pr + 1 in x and y).
+    __device__ __forceinline__ void v_values(int p, u32 magic, h2 (&vals)[Sh::NKV / 2][4]) const
+    {
+        const int k = p >> 1;
+        const bool second = p & 1;
+#pragma unroll
+        for (int pr = 0; pr < Sh::NKV / 2; ++pr) {
+            _Float16 s0, s1;
+            u32 a0, a1, b0, b1;
+            split_half_block(rv + 4 * (2 * pr), vb, s0, a0, a1);
+            split_half_block(rv + 4 * (2 * pr + 1), vb, s1, b0, b1);
+            const u32 x0 = k ? a1 : a0, x1 = k ? b1 : b0;
+            const u32 z = __builtin_amdgcn_perm(x1, x0, second ? 0x07060302u : 0x05040100u);
+            q4_unpack_ao(z, magic, vals[pr]);
+            const h2 s2 = {s0, s1};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) vals[pr][t] = vals[pr][t] * s2;
+        }
+    }
+
     // V piece p: for NKV >= 2, code dword k = p >> 1 and element half
     // (p & 1 ? the "b" bytes : the "a" bytes) of all NKV keys
     __device__ __forceinline__ void v_piece(int p, _Float16 *vt, u32 magic) const
@@ -244,19 +267,7 @@ struct Q4Loader {
             const bool second = p & 1;
             const int e0 = 8 * vh + 4 * k;
             h2 vals[Sh::NKV / 2][4];
-#pragma unroll
-            for (int pr = 0; pr < Sh::NKV / 2; ++pr) {
-                _Float16 s0, s1;
-                u32 a0, a1, b0, b1;
-                split_half_block(rv + 4 * (2 * pr), vb, s0, a0, a1);
-                split_half_block(rv + 4 * (2 * pr + 1), vb, s1, b0, b1);
-                const u32 x0 = k ? a1 : a0, x1 = k ? b1 : b0;
-                const u32 z = __builtin_amdgcn_perm(x1, x0, second ? 0x07060302u : 0x05040100u);
-                q4_unpack_ao(z, magic, vals[pr]);
-                const h2 s2 = {s0, s1};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) vals[pr][t] = vals[pr][t] * s2;
-            }
+            v_values(p, magic, vals);
             // element of vals[*][t]: a-bytes give e0, e0+1, e0+16, e0+17;
             // b-bytes give e0+2, e0+3, e0+18, e0+19. One per-thread base
             // (block, half, key position), the rest immediate offsets.

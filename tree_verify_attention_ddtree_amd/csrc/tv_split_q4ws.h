@@ -25,8 +25,9 @@
 //   load wave q (4..7)   moves the raw Q4_0 bytes of chunk c + 3 from HBM
 //                        into registers and dequantises chunk c + 1 into
 //                        the other LDS stage: keys 16q .. 16q + 15 of K over
-//                        all of D, and D-quarter q of V (rows 64q .. 64q + 63
-//                        of V^T) over all 64 keys. It also runs the NSH
+//                        all of D (K fragments 8q .. 8q + 7), and D-quarter
+//                        q of V over all 64 keys (V^T fragments 8q .. 8q +
+//                        7). It also runs the NSH
 //                        shared tiles: their scores over key tile q of each
 //                        chunk and their PV over D-quarter q.
 //
@@ -42,10 +43,10 @@
 //           flagged one) and its PV from stage st ^ 1, V^T quarter q; scores
 //           of chunk c over key tile q from stage st, P quarter to the
 //           exchange buffer of parity st;
-//           dequantise chunk c + 1 into stage st ^ 1 (K rows 16q.., V^T rows
-//           64q..); request the raw bytes of chunk c + 3.
-// Every LDS region a load wave writes in iteration i (stage st ^ 1: K rows
-// 16q.., V^T rows 64q..) was last read by the math waves in iteration i - 1
+//           dequantise chunk c + 1 into stage st ^ 1 (K and V^T fragments
+//           8q .. 8q + 7); request the raw bytes of chunk c + 3.
+// Every LDS region a load wave writes in iteration i (stage st ^ 1: K and
+// V^T fragments 8q .. 8q + 7) was last read by the math waves in iteration i - 1
 // (before the barrier) and by that load wave itself earlier in iteration i;
 // the math waves read it again only after the next barrier. The shared
 // tiles' exchange buffers alternate with the parity, as the stages do.
@@ -61,13 +62,36 @@ namespace tv {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// One LDS stage of a dequantised 64-key chunk (head_dim 256), in MFMA
+// fragment order, so that every fragment read of a wave is one contiguous
+// 1 KB (K) or four contiguous 256-byte rows (V^T), and the load waves'
+// stores meet no bank conflict:
+//   K: 32 fragments of 512 halves, fragment 8 t + b = keys 16t .. 16t + 15
+//      and block b (values 32b .. 32b + 31); slot c + 16 g (8 halves) holds
+//      key 16t + c, values 32b + 8g .. + 7 (the A operand of S^T = K Q^T);
+//   V^T: 32 fragments of VFRAG halves, fragment 2j + kk = values 16j .. 16j
+//      + 15 and k-step kk (keys 32kk .. 32kk + 31); row g (VROW halves: 16
+//      slots and 16 bytes of padding) slot c holds value 16j + c of keys
+//      32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3) (the A operand of
+//      O^T += V^T P^T, in the key order of the P^T fragments). The padding
+//      puts the 32 eight-byte pieces of a load wave's store (one value, 4
+//      keys each) in distinct banks.
+struct FmStage {
+    static constexpr int KFRAG = 512;
+    static constexpr int KELEMS = 32 * KFRAG;
+    static constexpr int VROW = 136;
+    static constexpr int VFRAG = 4 * VROW;
+    static constexpr int VELEMS = 32 * VFRAG;
+    static constexpr int ELEMS = KELEMS + VELEMS;
+};
+
 // LDS of a split workgroup (module-scope arrays; each kernel that uses them
 // gets its own): the two K / V^T stages (the query rows are staged there
 // first and the normalised output rows gathered there last) and the shared
 // tiles' exchange, by chunk parity: P^T fragments ([k-step][lane], 8 halves)
 // of up to two shared tiles, the maximum each load wave's key tile was taken
 // against, the rescale flags.
-constexpr int kWsLdsElems = 2 * Stage<256, TV_KV_Q4_0, true, true>::ELEMS;
+constexpr int kWsLdsElems = 2 * FmStage::ELEMS;
 static __shared__ __attribute__((aligned(16))) _Float16 ws_lds[kWsLdsElems];
 static __shared__ __attribute__((aligned(16))) _Float16 ws_psh[2][2][2 * 64 * 8];
 static __shared__ float ws_shmax[2][2][4][16];
@@ -83,12 +107,10 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                                          uint32_t *ticket, uint32_t &next)
 {
     constexpr int D = 256;
-    // K rows at 544 bytes (an S^T fragment read meets no bank conflict),
-    // V^T rows at 160 bytes
-    using St = Stage<D, TV_KV_Q4_0, true, true>;
+    using St = FmStage;
     using L = Q4Loader<D, true, true>;
     using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH, kWsThreads>;
-    constexpr int NB = St::NB;     // 32-value blocks per row
+    constexpr int NB = D / 32;     // 32-value blocks per row
     constexpr int NDT = D / 16;    // D tiles
     constexpr int NDQ = NDT / 4;   // D tiles of a quarter
     constexpr int NSX = NSH > 0 ? NSH : 1;
@@ -151,16 +173,14 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             constexpr int st = decltype(stc)::value;
             __syncthreads();
             if (!live) return;
-            const _Float16 *ks = ws_lds + st * St::ELEMS;
-            const _Float16 *vt = ks + St::KELEMS;
+            const _Float16 *ks = ws_lds + st * St::ELEMS + 8 * lane;
+            const _Float16 *vt = ws_lds + st * St::ELEMS + St::KELEMS + grp * St::VROW + 8 * col;
             // K fragment ii of half kk: key tile 2kk + (ii & 1), block ii >> 1;
             // V fragment j of half kk: D tile j, k-step kk
             auto kfrag = [&](int kk, int ii) -> h8 {
-                return *(const h8 *)(ks + (16 * (2 * kk + (ii & 1)) + col) * St::KSTR + 32 * (ii >> 1) + 8 * grp);
+                return *(const h8 *)(ks + (8 * (2 * kk + (ii & 1)) + (ii >> 1)) * St::KFRAG);
             };
-            auto vfrag = [&](int kk, int j) -> h8 {
-                return *(const h8 *)(vt + (16 * j + col) * St::VSTR + 32 * kk + 8 * grp);
-            };
+            auto vfrag = [&](int kk, int j) -> h8 { return *(const h8 *)(vt + (2 * j + kk) * St::VFRAG); };
             // Each fragment read feeds NOWN MFMAs, so the four math waves
             // keep the LDS busy: reads stream through 4-entry rings, three
             // ahead of use, and run on across phases (the PV's first V
@@ -285,11 +305,40 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) qs[u][bb] = QS::frag(ws_lds, 16 * (4 * NOWN + u), col, grp, bb);
         __syncthreads();
+        // Stage stores of this lane: K pieces j (block 2u + (j >> 2), values
+        // 8 (j & 3) ..) of key 16q + (lane & 15) go to fragment 8q + 2u + (j >> 2),
+        // slot (lane & 15) + 16 (j & 3); V pieces (4 keys kappa = 4 (lane & 15)
+        // .. + 3: k-step kappa >> 5, row (kappa >> 2) & 3, half (kappa >> 4) & 1)
+        // of value 32 vb + 8 vh + e go to fragment 2 ((32 vb + 8 vh + e) >> 4)
+        // + (kappa >> 5), slot (8 vh + e) & 15.
+        const int kq = lane & 15;
+        const int ksto = (8 * q + 2 * (lane >> 4)) * St::KFRAG + 8 * kq;
+        const int vsto = St::KELEMS + (4 * ld0.vb + (kq >> 3)) * St::VFRAG + (kq & 3) * St::VROW + 64 * ld0.vh +
+                         4 * ((kq >> 2) & 1);
+        auto deq = [&](const L &ld, _Float16 *stg) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                int b, g;
+                const h8 o = ld.k_values(j, magic, b, g);
+                *(h8 *)(stg + ksto + (j >> 2) * St::KFRAG + 128 * (j & 3)) = o;
+            }
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+                h2 vals[2][4];
+                ld.v_values(pc, magic, vals);
+                // element e = 4 (pc >> 1) + 2 (pc & 1) + {0, 1, 16, 17}[t]
+                const int de = 4 * (pc >> 1) + 2 * (pc & 1);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    h4 w4;
+                    w4.s01 = vals[0][t];
+                    w4.s23 = vals[1][t];
+                    *(h4 *)(stg + vsto + (t >> 1) * 2 * St::VFRAG + 8 * (de + (t & 1))) = w4;
+                }
+            }
+        };
         // chunk c_begin into stage 0; its raw registers then take chunk c_begin + 2
-#pragma unroll
-        for (int j = 0; j < NB; ++j) ld0.k_piece(j, ws_lds, magic);
-#pragma unroll
-        for (int p = 0; p < L::V_PIECES; ++p) ld0.v_piece(p, ws_lds + St::KELEMS, magic);
+        deq(ld0, ws_lds);
         ld0.load_k_ws(chunk_row<false>(a, c_begin + 2), 2 < nch);
         ld0.load_v(chunk_row<false>(a, c_begin + 2), 2 < nch);
 
@@ -351,12 +400,12 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             }
 #pragma unroll
             for (int u = 0; u < NSH; ++u) lsh[u] += add_pair(psv[u][0], add_pair(psv[u][1], 0.f));
-            const _Float16 *vt = ws_lds + sp * St::ELEMS + St::KELEMS;
+            const _Float16 *vt = ws_lds + sp * St::ELEMS + St::KELEMS + grp * St::VROW + 8 * col;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int j = 0; j < NDQ; ++j) {
-                    const h8 vf = *(const h8 *)(vt + (16 * (NDQ * q + j) + col) * St::VSTR + 32 * kk + 8 * grp);
+                    const h8 vf = *(const h8 *)(vt + (2 * (NDQ * q + j) + kk) * St::VFRAG);
 #pragma unroll
                     for (int u = 0; u < NSH; ++u)
                         osh[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfs[u][kk], osh[u][j], 0, 0, 0);
@@ -369,13 +418,13 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             if (NSH > 0 && i < nch) {
                 if (i > 0) shared_pv(ic<st ^ 1>{});
                 // scores of key tile q of chunk c for the shared tiles
-                const _Float16 *kwb = ws_lds + st * St::ELEMS + (16 * q + col) * St::KSTR + 8 * grp;
+                const _Float16 *kwb = ws_lds + st * St::ELEMS + 8 * q * St::KFRAG + 8 * lane;
                 f4 ssh[NSX];
 #pragma unroll
                 for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) {
-                    const h8 kw = *(const h8 *)(kwb + 32 * bb);
+                    const h8 kw = *(const h8 *)(kwb + bb * St::KFRAG);
 #pragma unroll
                     for (int u = 0; u < NSH; ++u)
                         ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kw, qs[u][bb], ssh[u], 0, 0, 0);
@@ -413,12 +462,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             // st ^ 1, then request chunk c + 3 into the same registers
             _Float16 *ks_n = ws_lds + (st ^ 1) * St::ELEMS;
             auto next = [&](L &ldn) {
-                if (i + 1 < nch) {
-#pragma unroll
-                    for (int j = 0; j < NB; ++j) ldn.k_piece(j, ks_n, magic);
-#pragma unroll
-                    for (int p = 0; p < L::V_PIECES; ++p) ldn.v_piece(p, ks_n + St::KELEMS, magic);
-                }
+                if (i + 1 < nch) deq(ldn, ks_n);
                 ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
                 ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
             };

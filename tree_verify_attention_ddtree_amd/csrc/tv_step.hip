@@ -174,6 +174,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) step_kernel(const StepArgs s)
         const StepLayer &ly = s.layer[it.layer];
         const MergePtrs p = {ly.sp.q, ly.k_tree, ly.v_tree, ly.sp.ws_o, ly.sp.ws_m, ly.out, ly.sp.k_cache,
                              ly.sp.v_cache};
+        static_assert(2 * sizeof(MergeLds<256>) <= sizeof(ws_lds), "two merge rows in the split items' LDS");
         MergeLds<256> *ml = (MergeLds<256> *)ws_lds;
         const int half = tid >> 8;
         const int NR = s.ma.NR;
@@ -185,6 +186,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) step_kernel(const StepArgs s)
         }
     } else {
         // --------------------------------------------------- acceptance item
+        static_assert(2 * sizeof(AcceptLds) <= sizeof(ws_lds), "two acceptance slices in the split items' LDS");
         AcceptLds *al = (AcceptLds *)ws_lds;
         const int half = tid >> 8;
         const int f = 2 * it.index + half;
