@@ -68,7 +68,7 @@ struct Q4Share {
     static constexpr int RAWV = 4 * NKV;
 };
 
-template <int D, bool WIDE_V, bool WIDE_K = false>
+template <int D, bool WIDE_V>
 struct Q4Loader {
     using Sh = Q4Share<D>;
     static constexpr int NB = Sh::NB;
@@ -228,7 +228,7 @@ struct Q4Loader {
     {
         int b, g;
         const h8 o = k_values(j, magic, b, g);
-        *(h8 *)(ks + kk * Stage<D, TV_KV_Q4_0, WIDE_V, WIDE_K>::KSTR + 32 * b + 8 * g) = o;
+        *(h8 *)(ks + kk * Stage<D, TV_KV_Q4_0, WIDE_V>::KSTR + 32 * b + 8 * g) = o;
     }
 
     static constexpr int V_PIECES = Sh::NKV >= 2 ? 4 : 2;
@@ -260,7 +260,7 @@ struct Q4Loader {
     // (p & 1 ? the "b" bytes : the "a" bytes) of all NKV keys
     __device__ __forceinline__ void v_piece(int p, _Float16 *vt, u32 magic) const
     {
-        constexpr int VSTR = Stage<D, TV_KV_Q4_0, WIDE_V, WIDE_K>::VSTR;
+        constexpr int VSTR = Stage<D, TV_KV_Q4_0, WIDE_V>::VSTR;
         const int pos = vpos(Sh::NKV * kg);
         if constexpr (Sh::NKV >= 2) {
             const int k = p >> 1;

@@ -170,14 +170,12 @@ __device__ __forceinline__ int vpos(int kappa)
     return (kappa & ~31) + 8 * ((kappa & 15) >> 2) + 4 * ((kappa >> 4) & 1) + (kappa & 3);
 }
 
-template <int D, int KVT, bool WIDE_V = false, bool WIDE_K = false>
+template <int D, int KVT, bool WIDE_V = false>
 struct Stage {
     static constexpr int NB = D / 32;   // 32-wide blocks per row
     static constexpr int NK = NB / 2;   // keys per thread in a chunk (K or V)
-    // K row stride in LDS (halves): D + 8, or with WIDE_K D + 16 (an odd
-    // multiple of 32 bytes, at which an S^T fragment read of 16 rows x 4
-    // lane groups of 16 bytes meets no bank conflict)
-    static constexpr int KSTR = WIDE_K ? D + 16 : D + 8;
+    // K row stride in LDS (halves)
+    static constexpr int KSTR = D + 8;
     // V^T row stride in LDS (halves): 144 bytes, or with WIDE_V 160 bytes,
     // an odd multiple of 32, at which a PV fragment read (16 rows x 4 lane
     // groups of 16 bytes) meets no bank conflict. The Q4_0 kernels with

@@ -108,7 +108,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
 {
     constexpr int D = 256;
     using St = FmStage;
-    using L = Q4Loader<D, true, true>;
+    using L = Q4Loader<D, true>;  // its loads and decoding; the stage stores are this file's
     using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH, kWsThreads>;
     constexpr int NB = D / 32;     // 32-value blocks per row
     constexpr int NDT = D / 16;    // D tiles
