@@ -158,6 +158,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
 
         f4 o[NOWN][NDT];
         float m[NOWN], l[NOWN];
+        const float inv_c = 1.0f / a.c;
 #pragma unroll
         for (int k = 0; k < NOWN; ++k) {
             m[k] = kNegBig;
@@ -210,24 +211,28 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                 vr[1] = vfrag(kk, 1);
                 vr[2] = vfrag(kk, 2);
                 TV_SCHED_FENCE();
-                // running maxima over these 32 keys; one wave-uniform
-                // branch for the rare rescale
-                float mnew[NOWN];
+                // does a score of these 32 keys exceed its row's running
+                // maximum by more than kTau: each lane compares the largest
+                // of its 8 raw scores with the row's threshold (m + kTau) / c
+                // (c > 0); only the rare rescale, one wave-uniform branch,
+                // takes the row maxima across lanes
                 bool need = false;
+                float tl[NOWN];
 #pragma unroll
                 for (int k = 0; k < NOWN; ++k) {
                     const float t0 = fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3]));
                     const float t1 = fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3]));
-                    mnew[k] = xmax_16_32(fmaxf(t0, t1)) * a.c;
-                    need = need || (mnew[k] > m[k] + kTau);
+                    tl[k] = fmaxf(t0, t1);
+                    need = need || (tl[k] > (m[k] + kTau) * inv_c);
                 }
                 if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
                     for (int k = 0; k < NOWN; ++k) {
-                        const float mm = fmaxf(m[k], mnew[k]);
+                        const float mm = fmaxf(m[k], xmax_16_32(tl[k]) * a.c);
                         const float f = __builtin_amdgcn_exp2f(m[k] - mm);
                         l[k] *= f;
                         m[k] = mm;
+
 #pragma unroll
                         for (int j = 0; j < NDT; ++j) o[k][j] *= f;
                     }
@@ -344,6 +349,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
 
         f4 osh[NSX][NDQ];
         float msh[NSX], lsh[NSX], mown[NSX];
+        const float inv_c = 1.0f / a.c;
         h2 psv[NSX][2];
 #pragma unroll
         for (int u = 0; u < NSX; ++u) {
@@ -433,18 +439,24 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                 // + 3) against the common running maximum or, when some row
                 // of the key tile exceeds it by more than kTau (the flag),
                 // against the larger of the two, so that no P exceeds 2^kTau
+                // (each lane compares the largest of its raw scores with
+                // (m + kTau) / c; the row maxima across lanes only when flagged)
                 bool need_sh = false;
-                float mnew[NSX];
+                float tl[NSX], mws[NSX];
 #pragma unroll
                 for (int u = 0; u < NSH; ++u) {
-                    const float t = fmaxf(fmaxf(ssh[u][0], ssh[u][1]), fmaxf(ssh[u][2], ssh[u][3]));
-                    mnew[u] = xmax_16_32(t) * a.c;
-                    need_sh = need_sh || (mnew[u] > msh[u] + kTau);
+                    tl[u] = fmaxf(fmaxf(ssh[u][0], ssh[u][1]), fmaxf(ssh[u][2], ssh[u][3]));
+                    need_sh = need_sh || (tl[u] > (msh[u] + kTau) * inv_c);
+                    mws[u] = msh[u];
                 }
                 const bool flag = __builtin_amdgcn_ballot_w64(need_sh) != 0;
+                if (flag) {
+#pragma unroll
+                    for (int u = 0; u < NSH; ++u) mws[u] = fmaxf(msh[u], xmax_16_32(tl[u]) * a.c);
+                }
 #pragma unroll
                 for (int u = 0; u < NSH; ++u) {
-                    const float mw = flag ? fmaxf(msh[u], mnew[u]) : msh[u];
+                    const float mw = mws[u];
                     mown[u] = mw;
                     psv[u][0] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][0], a.c, -mw)),
                                        __builtin_amdgcn_exp2f(__builtin_fmaf(ssh[u][1], a.c, -mw)));
