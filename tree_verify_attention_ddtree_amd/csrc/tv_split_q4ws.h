@@ -250,7 +250,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                         p[t] = pk_rtz(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0], a.c, -m[k])),
                                       __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i0 + 1], a.c, -m[k])));
                     }
-                    l[k] += add_pair(p[0], add_pair(p[1], 0.f)) + add_pair(p[2], add_pair(p[3], 0.f));
+                    l[k] = add_pair(p[3], add_pair(p[2], add_pair(p[1], add_pair(p[0], l[k]))));
                     h8 fr;
                     fr.s01 = p[0];
                     fr.s23 = p[1];
@@ -405,7 +405,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                 }
             }
 #pragma unroll
-            for (int u = 0; u < NSH; ++u) lsh[u] += add_pair(psv[u][0], add_pair(psv[u][1], 0.f));
+            for (int u = 0; u < NSH; ++u) lsh[u] = add_pair(psv[u][1], add_pair(psv[u][0], lsh[u]));
             const _Float16 *vt = ws_lds + sp * St::ELEMS + St::KELEMS + grp * St::VROW + 8 * col;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
