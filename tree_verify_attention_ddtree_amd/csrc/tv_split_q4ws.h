@@ -367,9 +367,10 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
         // and each quarter is scaled to it in fp16; this wave's own quarter
         // (as used) goes into its row sums; then the PV of that chunk over
         // D-quarter q from its stage.
-        auto shared_update = [&](auto spc, h8 (&pfs)[NSX][2]) {
+        auto shared_pv = [&](auto spc) {
             constexpr int sp = decltype(spc)::value;
             const u4v fl = *(const u4v *)ws_shflag[sp];
+            h8 pfs[NSX][2];
 #pragma unroll
             for (int u = 0; u < NSH; ++u) {
                 pfs[u][0] = *(const h8 *)(&ws_psh[sp][u][0] + lane * 8);
@@ -405,9 +406,6 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             }
 #pragma unroll
             for (int u = 0; u < NSH; ++u) lsh[u] = add_pair(psv[u][1], add_pair(psv[u][0], lsh[u]));
-        };
-        auto shared_mfma = [&](auto spc, const h8 (&pfs)[NSX][2]) {
-            constexpr int sp = decltype(spc)::value;
             const _Float16 *vt = ws_lds + sp * St::ELEMS + St::KELEMS + grp * St::VROW + 8 * col;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -419,38 +417,15 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                         osh[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfs[u][kk], osh[u][j], 0, 0, 0);
                 }
         };
-        auto shared_pv = [&](auto spc) {
-            h8 pfs[NSX][2];
-            shared_update(spc, pfs);
-            shared_mfma(spc, pfs);
-        };
 
-        // Iteration i (chunk c): the shared tiles' exchange of chunk c - 1
-        // (and the rare rescale) first; then, in one branch-free stretch so
-        // that the scheduler can interleave them, the shared PV of chunk c - 1
-        // and the shared scores of chunk c (MFMAs and their LDS reads) with
-        // the dequantisation of chunk c + 1 (vector work) and the requests of
-        // chunk c + 3; then the shared softmax of chunk c and its exchange.
-        // Past the split's end the dequantisation decodes the zeros of an
-        // empty descriptor into the stage no one reads again.
-        auto body = [&](auto stc, auto firstc, int i) {
+        auto body = [&](auto stc, int i) {
             constexpr int st = decltype(stc)::value;
-            constexpr bool first = decltype(firstc)::value;
             __syncthreads();
-            L &ldn = st == 0 ? ld1 : ld0;  // raw bytes of chunk c + 1
-            if (i >= nch) {
-                // past the last chunk: the same requests, through an empty descriptor
-                ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), false);
-                ldn.load_v(chunk_row<false>(a, c_begin + i + 3), false);
-                return;
-            }
-            h8 pfs[NSX][2];
-            if constexpr (NSH > 0 && !first) shared_update(ic<st ^ 1>{}, pfs);
-            if constexpr (NSH > 0 && !first) shared_mfma(ic<st ^ 1>{}, pfs);
-            f4 ssh[NSX];
-            if constexpr (NSH > 0) {
+            if (NSH > 0 && i < nch) {
+                if (i > 0) shared_pv(ic<st ^ 1>{});
                 // scores of key tile q of chunk c for the shared tiles
                 const _Float16 *kwb = ws_lds + st * St::ELEMS + 8 * q * St::KFRAG + 8 * lane;
+                f4 ssh[NSX];
 #pragma unroll
                 for (int u = 0; u < NSH; ++u) ssh[u] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -460,13 +435,6 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                     for (int u = 0; u < NSH; ++u)
                         ssh[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kw, qs[u][bb], ssh[u], 0, 0, 0);
                 }
-            }
-            // chunk c + 1 into stage st ^ 1, then the request of chunk c + 3
-            // into the same registers
-            deq(ldn, ws_lds + (st ^ 1) * St::ELEMS);
-            ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
-            ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
-            if constexpr (NSH > 0) {
                 // this wave's P^T quarter (k-step q / 2, elements 4 (q & 1) ..
                 // + 3) against the common running maximum or, when some row
                 // of the key tile exceeds it by more than kTau (the flag),
@@ -502,6 +470,18 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                 }
                 if (lane == 0) ws_shflag[st][q] = flag;
             }
+            // dequantise chunk c + 1 (raw bytes of parity st ^ 1) into stage
+            // st ^ 1, then request chunk c + 3 into the same registers
+            _Float16 *ks_n = ws_lds + (st ^ 1) * St::ELEMS;
+            auto next = [&](L &ldn) {
+                if (i + 1 < nch) deq(ldn, ks_n);
+                ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
+                ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
+            };
+            if constexpr (st == 0)
+                next(ld1);
+            else
+                next(ld0);
         };
         // Both bodies run on every pass, the second past the last chunk too
         // (then it only requests nothing through an empty descriptor and
@@ -509,12 +489,10 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
         // the same loads in the same order and each wait counts only the
         // chunk it needs: with an odd last pass skipped, the wait counts at
         // the loop header had to cover both histories and waited for every
-        // load in flight. The first pass has no previous chunk to update.
-        body(ic<0>{}, std::true_type{}, 0);
-        body(ic<1>{}, std::false_type{}, 1);
-        for (int i = 2; i < nch; i += 2) {
-            body(ic<0>{}, std::false_type{}, i);
-            body(ic<1>{}, std::false_type{}, i + 1);
+        // load in flight.
+        for (int i = 0; i < nch; i += 2) {
+            body(ic<0>{}, i);
+            body(ic<1>{}, i + 1);
         }
         __syncthreads();  // E1: the last chunk's exchange is complete
         // the last chunk's shared update and PV; this wave's row sums meet
