@@ -3,7 +3,9 @@
 A step is the whole hot path on one batch of synthetic input: one layer of
 tree-verify attention for a budget-22 tree (23 nodes) over a 128K-row Q4_0
 KV cache (24 query / 4 KV heads, head_dim 256, no window), then greedy
-acceptance over 23 x 152000 fp32 logits. Inputs are resident in HBM before
+acceptance over 23 x 152000 fp32 logits, as one tree_verify_step call (two
+launches for one layer: the split kernel, then the merge rows and the
+acceptance slices side by side). Inputs are resident in HBM before
 the timed region; the KV cache rotates over enough copies (>= 1 GiB) that
 the 256 MB Infinity Cache cannot hold it between steps.
 
@@ -21,6 +23,7 @@ steps, so that the headline is taken on a device at its steady clocks.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -431,17 +434,18 @@ def main():
         attn(i)
         accept()
 
-    # the step: the attention launch (split and merge kernels), then the
-    # acceptance launch. (The same step as one launch of the work-queue
-    # kernel, tree_verify_step, is timed beside it: 2-3% slower for one
-    # layer, where the split items fill the device once and the merges run as
-    # items of one workgroup per compute unit.)
-    step = step_separate
+    # the step: tree_verify_step over the layer and the acceptance (for one
+    # layer two launches: the split kernel, then the merge rows and the
+    # acceptance slices side by side in one kernel). The same step as the
+    # separate calls (tree_verify_attn, then tree_accept: three launches) is
+    # timed beside it.
     sws = torch.zeros(tv.tv_step_workspace_bytes(desc, 1, vocab), dtype=torch.uint8, device=dev)
     step_arrs = [tv.step_layers([(kc, vc, q, kt, vt, out)]) for kc, vc in caches]
 
     def step_one(i):
         tv.tree_verify_step(desc, step_arrs[i % n_copies], lg, tokens, am, res, sws, stream)
+
+    step = step_one
 
     R = T
     kv_bytes = 2 * Hkv * R * (D // 32 * 18)
@@ -484,30 +488,38 @@ def main():
     # them, 200 steps that settle the device after the per-workload records
     # (which allocate and free gigabytes: a short bracket right after that ran
     # 10-20% slow).
+    # No garbage collection from here to the end of the timed runs: a
+    # collection pass is a host stall of milliseconds, which a short run
+    # cannot hide. (The collection it replaces runs first, before the
+    # warm-up: taken between the warm-up and a short timed run, its pause
+    # left the device idle long enough that a 20-step run took 15% longer.)
+    gc.collect()
+    gc.disable()
     if not args.no_configs:
         for i in range(200):
             step(i)
+    res.fill_(-1)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    res.fill_(-1)
     ms_step = timed(torch, stream, step, args.steps)
     assert int(res[0].item()) == planted_L
-    # the parts of a step on their own (medians of six runs of 50), and the
-    # one-launch form
+    # the parts of a step on their own and the step as separate calls
+    # (medians of six runs of 50)
     ms_attn = timed_median(torch, stream, attn, max(args.steps, 300))
     ms_accept = timed_median(torch, stream, lambda i: accept(), max(args.steps, 300))
-    ms_sep = timed_median(torch, stream, step, max(args.steps, 300))
+    ms_med = timed_median(torch, stream, step, max(args.steps, 300))
     res.fill_(-1)
-    timed(torch, stream, step_one, 50)
-    ms_one = timed_median(torch, stream, step_one, max(args.steps, 300))
+    timed(torch, stream, step_separate, 50)
+    ms_sep = timed_median(torch, stream, step_separate, max(args.steps, 300))
     assert int(res[0].item()) == planted_L
-    log(f"headline: {ms_step * 1e3:.1f} us per step ({ms_sep * 1e3:.1f} us median), attention {ms_attn * 1e3:.1f} us, "
-        f"one launch {ms_one * 1e3:.1f} us")
+    gc.enable()
+    log(f"headline: {ms_step * 1e3:.1f} us per step ({ms_med * 1e3:.1f} us median), attention {ms_attn * 1e3:.1f} us, "
+        f"separate calls {ms_sep * 1e3:.1f} us")
 
     kv_gbps = kv_bytes / (ms_attn * 1e-3) / 1e9
     tflops = flops / (ms_attn * 1e-3) / 1e12
-    tflops_one = flops / (ms_one * 1e-3) / 1e12
+    tflops_sep = flops / (ms_sep * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_step,
@@ -529,13 +541,14 @@ def main():
         },
         "kv_gbps": kv_gbps,
         "kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
-        "ms_per_step_median": ms_sep,
+        "ms_per_step_median": ms_med,
+        "step_plan": tv.tv_step_plan(desc, 1, vocab),
         "attn_us": ms_attn * 1e3,
         "accept_us": ms_accept * 1e3,
-        "one_launch_step": {
-            "ms_per_step": ms_one, "steps_per_s": 1e3 / ms_one, "tflops": tflops_one,
-            "frac_mfma": tflops_one / MFMA_FP16_PEAK_TFLOPS, "plan": tv.tv_step_plan(desc, 1, vocab),
-            "note": "tree_verify_step: split, merge and acceptance items of the step in one launch (median of six parts)",
+        "separate_calls": {
+            "ms_per_step": ms_sep, "steps_per_s": 1e3 / ms_sep, "tflops": tflops_sep,
+            "frac_mfma": tflops_sep / MFMA_FP16_PEAK_TFLOPS,
+            "note": "tree_verify_attn then tree_accept: three launches (median of six parts)",
         },
         "roofline": {
             "kernel": "tree_verify_attn launch: split_q4ws_kernel<2, 1> + merge_kernel<256>",

@@ -341,11 +341,13 @@ TV_API size_t tv_step_workspace_bytes(const tv_attn_desc *d, int32_t n_layers, i
 
 /* How tree_verify_step runs a shape (host only, launches nothing). */
 typedef struct tv_step_plan_info {
-    int32_t launches;   /* kernel launches per call: 1 with the work-queue kernel */
-    int32_t workgroups; /* workgroups of the work-queue kernel, 0 without it */
+    int32_t launches;   /* kernel launches per call: 1 with the work-queue kernel,
+                           2 for one layer of head_dim 256 with whole chunks */
+    int32_t workgroups; /* workgroups of the work-queue kernel, or of the two
+                           launches of one layer; 0 for the separate launches */
     int32_t splits;     /* key-range splits per KV head and row group of every layer */
     int32_t row_groups;
-    int64_t items;      /* work items: acceptance, split and merge items */
+    int64_t items;      /* work items of the work-queue kernel (0 without it) */
     uint64_t workspace_bytes;
 } tv_step_plan_info;
 
@@ -382,8 +384,12 @@ TV_API int tv_step_plan(const tv_attn_desc *d, int32_t n_layers, int32_t vocab, 
  *             valid) and which only the caller clears. Calls that share a
  *             workspace must not overlap.
  *
- * Where the plan's split kernel is TV_SPLIT_Q4_0_WS the step is one launch
- * of a persistent kernel (at most one workgroup per compute unit) that takes
+ * One layer of head_dim 256 with at least one whole chunk takes two
+ * launches: its split kernel (as in tree_verify_attn), then one kernel whose
+ * workgroups merge the output rows or scan the acceptance slices side by
+ * side (the merge and the acceptance do not depend on each other), which
+ * saves the acceptance its own launch. Otherwise, where the plan's split
+ * kernel is TV_SPLIT_Q4_0_WS, the step is one launch of a persistent kernel (at most one workgroup per compute unit) that takes
  * work items from a device-side queue in ticket order: the acceptance
  * slices, then every layer's split items, each layer's merge items queued
  * behind the next layer's splits. A merge item waits (a bounded spin) for

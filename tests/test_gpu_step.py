@@ -117,7 +117,8 @@ def _same_tree(inps):
 
 
 # (H_q, H_kv, D, n_ctx, n, window, kv, layers, vocab, single launch: True,
-# False, or None where the plan decides). The single-launch shapes cover
+# False, or None where the plan decides; for one layer of head_dim 256 the
+# launches the plan must make). The single-launch shapes cover
 # every tile layout of the work-queue kernel: M = 6 n query rows per KV head
 # in T = ceil(M / 16) tiles; T = 9 -> (2, 1), 4 -> (1, 0), 5 -> (1, 1),
 # 6 -> (1, 2), 8 -> (2, 0).
@@ -134,6 +135,10 @@ SHAPES = [
     (24, 4, 256, 50, 23, 0, "q4_0", 2, 64, False),            # no whole chunk: merge only
     (8, 2, 128, 3000, 12, 0, "f16", 2, 3000, False),          # F16, head_dim 128
     (4, 2, 256, 1000, 8, 0, "q4_0", 2, 1024, False),          # one tile (all shared)
+    (24, 4, 256, 4096, 23, 0, "q4_0", 1, 152000, 2),          # one layer: split, then merge + acceptance
+    (24, 4, 256, 4096 + 37, 23, 0, "q4_0", 1, 5000, 2),       # one layer, masked split kernel
+    (8, 2, 256, 3000, 12, 0, "f16", 1, 3000, 2),              # one layer, F16
+    (8, 2, 128, 3000, 12, 0, "f16", 1, 3000, 3),              # one layer, head_dim 128: separate launches
 ]
 
 
@@ -144,7 +149,8 @@ def test_step_equals_separate_calls(shape):
     inps = _same_tree([synth.attn_inputs(**dict(w, seed=9100 + 7 * l + T)) for l in range(L)])
     for x in inps:
         x["window"] = W
-    plan = check_step(inps, vocab, 9200 + T, expect_launches=1 if single else None, oracle_layers=range(L))
+    expect = single if isinstance(single, int) and not isinstance(single, bool) else (1 if single else None)
+    plan = check_step(inps, vocab, 9200 + T, expect_launches=expect, oracle_layers=range(L))
     if single is False:
         assert plan["launches"] > 1 and plan["workgroups"] == 0
 

@@ -295,10 +295,11 @@ def test_step_argument_checks(L):
 
 
 def test_step_plan():
-    """One launch where the warp-specialised split kernel runs: one work item
-    per workgroup (acceptance items of two 8192-logit slices, split items,
-    merge items of 8 rows, 4 for the last layer); the separate launches
-    otherwise. The workspace is
+    """Several layers: one launch where the warp-specialised split kernel
+    runs, one work item per workgroup (acceptance items of two 8192-logit
+    slices, split items, merge items of 8 rows, 4 for the last layer); the
+    separate launches otherwise. One layer of head_dim 256: two launches.
+    The workspace is
     a 2048-byte header plus each layer's partials, rounded to 256 bytes."""
     Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
     par = [-1] + [i // 2 for i in range(22)]
@@ -308,11 +309,19 @@ def test_step_plan():
         d, keep = tv.make_desc(parent, 24, 4, D, kv, n_ctx, window, 0.0625, row, row * max(n_ctx, 1))
         return tv.tv_step_plan(d, L, vocab, 256), tv.tv_attn_plan(d, 256)
 
-    # one layer: the split count of tree_verify_attn
+    # one layer: the split count of tree_verify_attn, two launches (the split
+    # kernel, then the merge rows and acceptance slices side by side)
     p, a = plan(Q, 131072, 1, 152000)
     assert a["kernel"] == tv.TV_SPLIT_Q4_0_WS and a["splits"] == 64 and p["splits"] == 64
-    assert p["items"] == (23 * 19 + 1) // 2 + 64 * 4 + (23 * 24 + 3) // 4
+    assert (p["launches"], p["workgroups"], p["items"]) == (2, 64 * 4 + 23 * 24 + 23 * 19, 0)
     assert p["workspace_bytes"] == 2048 + (a["workspace_bytes"] + 255) // 256 * 256
+    # also for the other kernels of head_dim 256 (F16, two row groups)
+    p, a = plan(F, 8192, 1, 1000)
+    assert (p["launches"], p["workgroups"]) == (2, a["splits"] * 4 * a["row_groups"] + 23 * 24 + 23)
+    # one layer of head_dim 128, or without a whole chunk: the separate launches
+    for n_ctx, D in ((8192, 128), (50, 256)):
+        p, a = plan(Q, n_ctx, 1, 1000, D=D)
+        assert (p["workgroups"], p["items"]) == (0, 0) and p["launches"] == (2 if a["splits"] else 1) + 1
     # 16 layers at 32K: half the splits (at most 16 chunks per split item)
     p, a = plan(Q, 32768, 16, 152000)
     assert a["splits"] == 64 and (p["splits"], p["row_groups"]) == (32, 1)

@@ -237,7 +237,13 @@ void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int voc
     const int64_t n_last = (NR + kMergeRowsLast - 1) / kMergeRowsLast;
     const int64_t slices = (int64_t)d->n_nodes * (((int64_t)vocab + kSliceFloats - 1) / kSliceFloats);
     const int64_t total = (slices + 1) / 2 + n_layers * n_split + (n_layers - 1) * n_merge + n_last;
-    if (split_kernel_kind(d, p) == TV_SPLIT_Q4_0_WS && fits && total <= INT32_MAX) {
+    if (n_layers == 1 && d->head_dim == 256 && p.S > 0 && NR + slices <= INT32_MAX) {
+        // one layer: its split kernel, then its merge and the acceptance in
+        // one launch of 256-thread workgroups
+        *items = 0;
+        *workgroups = (int)(n_split + NR + slices);
+        *launches = 2;
+    } else if (split_kernel_kind(d, p) == TV_SPLIT_Q4_0_WS && fits && total <= INT32_MAX) {
         *items = total;
         *workgroups = (int)total;
         *launches = 1;

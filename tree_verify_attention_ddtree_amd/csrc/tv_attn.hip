@@ -567,8 +567,8 @@ void fill_merge_args(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPl
     }
 }
 
-int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
-                hipStream_t stream)
+// The split kernel of one layer (no launch when the plan has no split).
+int launch_split(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, hipStream_t stream)
 {
     const int D = d->head_dim;
     if (plan.S > 0) {
@@ -582,6 +582,15 @@ int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &p
         void *args[] = {(void *)&a};
         if (hipLaunchKernel((const void *)fn, grid, dim3(threads), args, 0, stream) != hipSuccess) return TV_E_HIP;
     }
+    return TV_OK;
+}
+
+int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws,
+                hipStream_t stream)
+{
+    const int D = d->head_dim;
+    const int rc = launch_split(d, p, plan, ws, stream);
+    if (rc) return rc;
     MergeArgs mg;
     fill_merge_args(d, p, plan, ws, &mg);
     const void *mfn = D == 64 ? (const void *)merge_kernel<64>

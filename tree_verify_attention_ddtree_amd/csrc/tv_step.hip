@@ -209,6 +209,26 @@ __global__ void __launch_bounds__(kWsThreads, 1) step_kernel(const StepArgs s)
     }
 }
 
+// One layer's merge and the acceptance in one launch (the step of a single
+// layer, after its split kernel): workgroups [0, NR) merge an output row
+// each, the rest scan one acceptance slice each (row-major over the rows'
+// slices). The two parts share nothing but the launch.
+__global__ void __launch_bounds__(256) merge_accept_kernel(const MergeArgs m, const AcceptArgs ac)
+{
+    static_assert(kAccThreads == 256, "a merge row and an acceptance slice take 256 threads each");
+    __shared__ union {
+        MergeLds<256> mg;
+        AcceptLds acc;
+    } sm;
+    const int b = blockIdx.x;
+    if (b < m.NR) {
+        merge_row<256>(m, m.p, b, threadIdx.x, true, sm.mg);
+        return;
+    }
+    const int f = b - m.NR;
+    accept_slice(ac, f / ac.n_slices, f % ac.n_slices, threadIdx.x, true, sm.acc);
+}
+
 // step kernel of a tile layout (every layout ws_layout accepts)
 static const void *pick_step(int nown, int nsh)
 {
@@ -220,6 +240,7 @@ static const void *pick_step(int nown, int nsh)
 }
 
 int launch_attn(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, hipStream_t stream);
+int launch_split(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, hipStream_t stream);
 int launch_accept(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
                   int32_t *argmax_out, int32_t *result_out, void *ws, hipStream_t stream);
 void fill_accept_args(const float *logits, int n, int vocab, const int32_t *parent, const int32_t *tokens,
@@ -234,6 +255,21 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
     int launches = 0, wgs = 0;
     int64_t items = 0;
     step_shape(d, plan, n_layers, vocab, &launches, &wgs, &items);
+    if (launches == 2) {
+        // one layer: its split kernel, then its merge and the acceptance in
+        // one launch
+        const int rc = launch_split(d, &layers[0], plan, base + kStepHeader, stream);
+        if (rc) return rc;
+        MergeArgs m;
+        AcceptArgs ac;
+        fill_merge_args(d, &layers[0], plan, base + kStepHeader, &m);
+        fill_accept_args(logits, d->n_nodes, vocab, d->parent, tokens, argmax_out, result_out, base + kQAccept, &ac);
+        void *args[] = {(void *)&m, (void *)&ac};
+        const int nwg = m.NR + ac.n * ac.n_slices;
+        if (hipLaunchKernel((const void *)merge_accept_kernel, dim3(nwg), dim3(256), args, 0, stream) != hipSuccess)
+            return TV_E_HIP;
+        return TV_OK;
+    }
     if (wgs == 0) {
         // per-layer launches, then the acceptance, on the same stream
         for (int l = 0; l < n_layers; ++l) {
