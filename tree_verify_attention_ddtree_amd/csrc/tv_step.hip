@@ -210,9 +210,11 @@ __global__ void __launch_bounds__(kWsThreads, 1) step_kernel(const StepArgs s)
 }
 
 // One layer's merge and the acceptance in one launch (the step of a single
-// layer, after its split kernel): workgroups [0, NR) merge an output row
-// each, the rest scan one acceptance slice each (row-major over the rows'
-// slices). The two parts share nothing but the launch.
+// layer, after its split kernel): the first n * n_slices workgroups scan one
+// acceptance slice each (row-major over the rows' slices), the rest merge an
+// output row each. The two parts share nothing but the launch; the
+// acceptance, the longer chain of the two, is dispatched first (128K layer:
+// 97.9 against 99.2 us a step).
 __global__ void __launch_bounds__(256) merge_accept_kernel(const MergeArgs m, const AcceptArgs ac)
 {
     static_assert(kAccThreads == 256, "a merge row and an acceptance slice take 256 threads each");
@@ -221,12 +223,12 @@ __global__ void __launch_bounds__(256) merge_accept_kernel(const MergeArgs m, co
         AcceptLds acc;
     } sm;
     const int b = blockIdx.x;
-    if (b < m.NR) {
-        merge_row<256>(m, m.p, b, threadIdx.x, true, sm.mg);
+    const int na = ac.n * ac.n_slices;
+    if (b >= na) {
+        merge_row<256>(m, m.p, b - na, threadIdx.x, true, sm.mg);
         return;
     }
-    const int f = b - m.NR;
-    accept_slice(ac, f / ac.n_slices, f % ac.n_slices, threadIdx.x, true, sm.acc);
+    accept_slice(ac, b / ac.n_slices, b % ac.n_slices, threadIdx.x, true, sm.acc);
 }
 
 // step kernel of a tile layout (every layout ws_layout accepts)
