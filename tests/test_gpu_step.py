@@ -139,6 +139,8 @@ SHAPES = [
     (24, 4, 256, 4096 + 37, 23, 0, "q4_0", 1, 5000, 2),       # one layer, masked split kernel
     (8, 2, 256, 3000, 12, 0, "f16", 1, 3000, 2),              # one layer, F16
     (8, 2, 128, 3000, 12, 0, "f16", 1, 3000, 3),              # one layer, head_dim 128: separate launches
+    (24, 4, 256, 50, 23, 0, "q4_0", 1, 64, 2),                # one layer, no whole chunk: merge, acceptance
+    (8, 2, 128, 40, 12, 0, "f16", 1, 3000, 2),                # the same at head_dim 128
 ]
 
 

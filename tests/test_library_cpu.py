@@ -319,7 +319,7 @@ def test_step_plan():
     p, a = plan(F, 8192, 1, 1000)
     assert (p["launches"], p["workgroups"]) == (2, a["splits"] * 4 * a["row_groups"] + 23 * 24 + 23)
     # one layer of head_dim 128, or without a whole chunk: the separate launches
-    for n_ctx, D in ((8192, 128), (50, 256)):
+    for n_ctx, D in ((8192, 128), (50, 256), (40, 128)):
         p, a = plan(Q, n_ctx, 1, 1000, D=D)
         assert (p["workgroups"], p["items"]) == (0, 0) and p["launches"] == (2 if a["splits"] else 1) + 1
     # 16 layers at 32K: half the splits (at most 16 chunks per split item)

@@ -226,8 +226,8 @@ size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers)
 // Launches of one step call (1 with the work-queue kernel) and its work
 // items (one workgroup each); 0 workgroups when the plan has no work-queue
 // kernel (then the step makes the separate launches).
-void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
-                int64_t *items)
+StepForm step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
+                    int64_t *items)
 {
     // (the merge items address a layer's partials with 31-bit offsets)
     const bool fits = (int64_t)p.S * d->n_nodes * d->n_q_heads * (2 * d->head_dim) < ((int64_t)1 << 31);
@@ -243,15 +243,18 @@ void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int voc
         *items = 0;
         *workgroups = (int)(n_split + NR + slices);
         *launches = 2;
-    } else if (split_kernel_kind(d, p) == TV_SPLIT_Q4_0_WS && fits && total <= INT32_MAX) {
+        return kStepTwo;
+    }
+    if (split_kernel_kind(d, p) == TV_SPLIT_Q4_0_WS && fits && total <= INT32_MAX) {
         *items = total;
         *workgroups = (int)total;
         *launches = 1;
-    } else {
-        *items = 0;
-        *workgroups = 0;
-        *launches = n_layers * (p.S > 0 ? 2 : 1) + 1;
+        return kStepQueue;
     }
+    *items = 0;
+    *workgroups = 0;
+    *launches = n_layers * (p.S > 0 ? 2 : 1) + 1;
+    return kStepSeparate;
 }
 
 int device_cu_count(int *n_cu)

@@ -79,8 +79,12 @@ int device_cu_count(int *n_cu);
 // its merge items (see tv_step.hip).
 size_t step_layer_bytes(const tv_attn_desc *d, const SplitPlan &p);
 size_t step_ws_bytes(const tv_attn_desc *d, const SplitPlan &p, int n_layers);
-void step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
-                int64_t *items);
+// How tree_verify_step runs: the separate per-layer launches, one launch of
+// the work-queue kernel, or (one layer of head_dim 256 with at least one
+// whole chunk) the split kernel then merge_accept_kernel.
+enum StepForm { kStepSeparate = 0, kStepQueue = 1, kStepTwo = 2 };
+StepForm step_shape(const tv_attn_desc *d, const SplitPlan &p, int n_layers, int vocab, int *launches, int *workgroups,
+                    int64_t *items);
 int step_lag(int n_cu, int n_split);
 
 }  // namespace tv

@@ -256,8 +256,8 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
     const size_t lb = step_layer_bytes(d, plan);
     int launches = 0, wgs = 0;
     int64_t items = 0;
-    step_shape(d, plan, n_layers, vocab, &launches, &wgs, &items);
-    if (launches == 2) {
+    const StepForm form = step_shape(d, plan, n_layers, vocab, &launches, &wgs, &items);
+    if (form == kStepTwo) {
         // one layer: its split kernel, then its merge and the acceptance in
         // one launch
         const int rc = launch_split(d, &layers[0], plan, base + kStepHeader, stream);
@@ -272,7 +272,7 @@ int launch_step(const tv_attn_desc *d, int n_layers, const tv_attn_ptrs *layers,
             return TV_E_HIP;
         return TV_OK;
     }
-    if (wgs == 0) {
+    if (form == kStepSeparate) {
         // per-layer launches, then the acceptance, on the same stream
         for (int l = 0; l < n_layers; ++l) {
             const int rc = launch_attn(d, &layers[l], plan, base + kStepHeader + l * lb, stream);
