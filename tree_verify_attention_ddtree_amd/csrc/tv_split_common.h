@@ -29,7 +29,10 @@ constexpr u32 kOffNone = 0x80000000u;
 
 // Cache-policy bit of a buffer store (its aux operand) that makes the store
 // coherent at device scope (sc1 on gfx950): complete, it is visible to every
-// workgroup of the device, with no L2 write-back.
+// workgroup of the device, with no L2 write-back. Every split kernel stores
+// its partial state this way, so that none of it is left dirty in the L2s
+// when the launch ends and the end-of-launch release has little to write back
+// (measured on gfx950: 0.5-1 us less per split-and-merge pair).
 constexpr int kCpolSc1 = 16;
 
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
@@ -451,9 +454,9 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
                 const bool valid = r < a.M;
                 const _Float16 v = (_Float16)(lsum > 0.f ? acc / lsum : 0.f);
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), rwo,
-                                                      valid ? rowi * (u32)(2 * D) + 2u * (u32)d : kOffNone, 0, 0);
+                                                      valid ? rowi * (u32)(2 * D) + 2u * (u32)d : kOffNone, 0, kCpolSc1);
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(mx, lsum)), rwm,
-                                                      valid && d == 0 ? rowi * 4u : kOffNone, 0, 0);
+                                                      valid && d == 0 ? rowi * 4u : kOffNone, 0, kCpolSc1);
             }
         }
         __syncthreads();  // the scratch is free again
@@ -470,7 +473,7 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
         const bool mwriter = tile[k] < t_end && r < a.M && grp == 0;
         const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(m[k], lt)), rwm,
-                                              mwriter ? rowi * 4u : kOffNone, 0, 0);
+                                              mwriter ? rowi * 4u : kOffNone, 0, kCpolSc1);
     }
     __syncthreads();
     {
@@ -483,7 +486,7 @@ __device__ __forceinline__ void write_partials(const SplitArgs &a, _Float16 *scr
 #pragma unroll
         for (int jj = 0; jj < QS::NQ; ++jj) {
             const u4v v = *(const u4v *)(src + jj * QS::RS * QS::QSTR);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nown_rows ? rw.off + part : kOffNone, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nown_rows ? rw.off + part : kOffNone, 0, kCpolSc1);
             rw.next();
         }
     }

@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
         const bool mwriter = tile[k] < tm.t_end && r < a.M && grp == 0 && (k < NOWN || w == 0);
         const u32 rowi = (u32)((r / a.G) * a.H_q + gkv * a.G + r % a.G);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, partial_lse2(m[k], lt)), rwm,
-                                              mwriter ? rowi * 4u : kOffNone, 0, 0);
+                                              mwriter ? rowi * 4u : kOffNone, 0, kCpolSc1);
     }
     __syncthreads();
     {
@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(256, 1) split_q4_kernel(const SplitArgs a)
 #pragma unroll
         for (int jj = 0; jj < QS::NQ; ++jj) {
             const u4v v = *(const u4v *)(src + jj * QS::RS * QS::QSTR);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nrows ? rw.off + part : kOffNone, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rwo, r0 + jj * QS::RS < nrows ? rw.off + part : kOffNone, 0, kCpolSc1);
             rw.next();
         }
     }

@@ -11,7 +11,8 @@ __global__ void __launch_bounds__(kWsThreads, 1) split_q4ws_kernel(const SplitAr
 {
     const SplitPtrs p = {a.k_cache, a.v_cache, a.q, a.ws_o, a.ws_m};
     uint32_t next = 0;
-    ws_split<NOWN, NSH>(a, p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, nullptr, next);
+    // partial state through device-coherent stores (see kCpolSc1)
+    ws_split<NOWN, NSH, kCpolSc1>(a, p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, nullptr, next);
 }
 
 split_fn pick_split_q4ws(int D, int nown, int nsh)
