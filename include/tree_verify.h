@@ -238,7 +238,7 @@ TV_API size_t tv_accept_workspace_bytes(int32_t n_nodes, int32_t vocab);
  *             again, so a workspace can be reused call after call on one
  *             stream. Calls that share a workspace must not overlap (one
  *             stream, or ordered streams).
- * One launch: every workgroup reduces one 8192-logit slice of one row into
+ * One launch: every workgroup reduces one 16384-logit slice of one row into
  * the row's maximum with device-scope atomics; the workgroup that completes
  * the last row runs the walk.
  */

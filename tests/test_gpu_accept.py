@@ -42,7 +42,7 @@ def test_full_vocab_planted_64_trees():
         assert check(logits, parent, tok)[0] == L
 
 
-@pytest.mark.parametrize("vocab", [1, 3, 7, 8191, 8192, 8193, 30001, 152000, 152003])
+@pytest.mark.parametrize("vocab", [1, 3, 7, 8191, 8192, 8193, 16383, 16384, 16385, 30001, 152000, 152003])
 def test_vocab_sizes(vocab):
     rng = np.random.default_rng(vocab)
     parent = synth.draft_tree(rng, 23, 16)

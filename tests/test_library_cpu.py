@@ -296,7 +296,7 @@ def test_step_argument_checks(L):
 
 def test_step_plan():
     """Several layers: one launch where the warp-specialised split kernel
-    runs, one work item per workgroup (acceptance items of two 8192-logit
+    runs, one work item per workgroup (acceptance items of two 16384-logit
     slices, split items, merge items of 8 rows, 4 for the last layer); the
     separate launches otherwise. One layer of head_dim 256: two launches.
     The workspace is
@@ -313,7 +313,7 @@ def test_step_plan():
     # kernel, then the merge rows and acceptance slices side by side)
     p, a = plan(Q, 131072, 1, 152000)
     assert a["kernel"] == tv.TV_SPLIT_Q4_0_WS and a["splits"] == 64 and p["splits"] == 64
-    assert (p["launches"], p["workgroups"], p["items"]) == (2, 64 * 4 + 23 * 24 + 23 * 19, 0)
+    assert (p["launches"], p["workgroups"], p["items"]) == (2, 64 * 4 + 23 * 24 + 23 * 10, 0)
     assert p["workspace_bytes"] == 2048 + (a["workspace_bytes"] + 255) // 256 * 256
     # also for the other kernels of head_dim 256 (F16, two row groups)
     p, a = plan(F, 8192, 1, 1000)
@@ -325,7 +325,7 @@ def test_step_plan():
     # 16 layers at 32K: half the splits (at most 16 chunks per split item)
     p, a = plan(Q, 32768, 16, 152000)
     assert a["splits"] == 64 and (p["splits"], p["row_groups"]) == (32, 1)
-    n_items = (23 * 19 + 1) // 2 + 16 * 32 * 4 + 15 * ((23 * 24 + 7) // 8) + (23 * 24 + 3) // 4
+    n_items = (23 * 10 + 1) // 2 + 16 * 32 * 4 + 15 * ((23 * 24 + 7) // 8) + (23 * 24 + 3) // 4
     assert (p["launches"], p["workgroups"], p["items"]) == (1, n_items, n_items)
     layer = 32 * 23 * 24 * (2 * 256 + 4)
     assert p["workspace_bytes"] == 2048 + 16 * ((layer + 255) // 256 * 256)

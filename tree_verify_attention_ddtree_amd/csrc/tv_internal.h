@@ -65,7 +65,7 @@ inline bool ws_layout(int D, int nown, int nsh)
 
 // Sizes the host side needs from the kernels' layouts.
 constexpr size_t kAcceptWsBytes = 832;  // acceptance state: counters, per-row maxima
-constexpr int kSliceFloats = 8192;      // logits per acceptance workgroup (slice)
+constexpr int kSliceFloats = 16384;     // logits per acceptance workgroup (slice)
 constexpr size_t kStepHeader = 2048;    // work-queue header of the step workspace
 constexpr int kMergeRowsMid = 8;        // output rows per step merge item (all but the last layer)
 constexpr int kMergeRowsLast = 4;       // ... of the last layer

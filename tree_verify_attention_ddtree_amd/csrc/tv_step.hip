@@ -28,7 +28,7 @@
 //   M_{L-g} .. M_{L-2}, A, M_{L-1}
 //                           the remaining merges (4 rows per item for the
 //                           last layer) around the acceptance items (one
-//                           8192-logit slice per half workgroup), so that
+//                           16384-logit slice per half workgroup), so that
 //                           the workgroups freed by the last splits have
 //                           work while the slowest of them finish.
 // The first wave of workgroups takes split items only: workgroups are handed
