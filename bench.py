@@ -112,11 +112,18 @@ def copy_calibration(nbytes, steps):
 # helpers
 
 
-def timed(torch, stream, fn, k):
-    """Average ms per call of fn(i), i = 0..k-1, with HIP events on `stream`."""
+def timed(torch, stream, fn, k, lead=0, lead_base=0):
+    """Average ms per call of fn(i), i = 0..k-1, with HIP events on `stream`.
+    With `lead`, that many untimed calls fn(lead_base + i) are queued after
+    the synchronisation and before the first event, so that the timed calls
+    find the device already running (an idle device restarts at lower
+    clocks: a bracket of 50 calls that starts idle reads several percent
+    slow)."""
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    for i in range(lead):
+        fn(lead_base + i)
     e0.record(stream)
     for i in range(k):
         fn(i)
@@ -126,12 +133,16 @@ def timed(torch, stream, fn, k):
 
 
 def timed_median(torch, stream, fn, k, parts=6):
-    """Median over `parts` back-to-back runs of k / parts calls each of the
-    average ms per call: a stall outside the kernels (seen once in a while on
-    a freshly allocated gigabyte, tens of ms in one run) moves one part, not
-    the figure."""
+    """Median over `parts` runs of k / parts calls each of the average ms per
+    call: a stall outside the kernels (seen once in a while on a freshly
+    allocated gigabyte, tens of ms in one run) moves one part, not the
+    figure. Each run is led by as many untimed calls (on other rotation
+    indices), so that it times the device in steady state: the per-kernel
+    figures (the roofline's launch time among them) then agree with the
+    profiler's kernel durations."""
     per = max(1, k // parts)
-    return float(np.median([timed(torch, stream, lambda i, j=j: fn(j * per + i), per) for j in range(parts)]))
+    return float(np.median([timed(torch, stream, lambda i, j=j: fn(j * per + i), per, lead=per,
+                                  lead_base=k + j * per + 3) for j in range(parts)]))
 
 
 def rotated_q4_0(torch, dev, n_kv, rows, row_bytes, seed):
@@ -505,7 +516,7 @@ def main():
     ms_step = timed(torch, stream, step, args.steps)
     assert int(res[0].item()) == planted_L
     # the parts of a step on their own and the step as separate calls
-    # (medians of six runs of 50)
+    # (medians of six runs of 50, each led by 50 untimed calls)
     ms_attn = timed_median(torch, stream, attn, max(args.steps, 300))
     ms_accept = timed_median(torch, stream, lambda i: accept(), max(args.steps, 300))
     ms_med = timed_median(torch, stream, step, max(args.steps, 300))
@@ -548,7 +559,7 @@ def main():
         "separate_calls": {
             "ms_per_step": ms_sep, "steps_per_s": 1e3 / ms_sep, "tflops": tflops_sep,
             "frac_mfma": tflops_sep / MFMA_FP16_PEAK_TFLOPS,
-            "note": "tree_verify_attn then tree_accept: three launches (median of six parts)",
+            "note": "tree_verify_attn then tree_accept: three launches (median of six runs of 50, each led by 50 untimed steps)",
         },
         "roofline": {
             "kernel": "tree_verify_attn launch: split_q4ws_kernel<2, 1> + merge_kernel<256>",
