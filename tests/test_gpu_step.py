@@ -124,7 +124,7 @@ def _same_tree(inps):
 # 6 -> (1, 2), 8 -> (2, 0).
 SHAPES = [
     (24, 4, 256, 4096, 23, 0, "q4_0", 3, 152000, True),
-    (24, 4, 256, 2048 + 64 * 5, 10, 0, "q4_0", 2, 8193, True),
+    (24, 4, 256, 2048 + 64 * 5, 10, 0, "q4_0", 2, 16385, True),      # last acceptance slice of one logit
     (24, 4, 256, 4096, 12, 0, "q4_0", 2, 2000, True),
     (24, 4, 256, 4096, 16, 0, "q4_0", 2, 4099, True),
     (24, 4, 256, 4096, 20, 0, "q4_0", 2, 1000, True),
@@ -136,7 +136,7 @@ SHAPES = [
     (8, 2, 128, 3000, 12, 0, "f16", 2, 3000, False),          # F16, head_dim 128
     (4, 2, 256, 1000, 8, 0, "q4_0", 2, 1024, False),          # one tile (all shared)
     (24, 4, 256, 4096, 23, 0, "q4_0", 1, 152000, 2),          # one layer: split, then merge + acceptance
-    (24, 4, 256, 4096 + 37, 23, 0, "q4_0", 1, 5000, 2),       # one layer, masked split kernel
+    (24, 4, 256, 4096 + 37, 23, 0, "q4_0", 1, 32769, 2),      # one layer, masked split kernel; 3 slices a row
     (8, 2, 256, 3000, 12, 0, "f16", 1, 3000, 2),              # one layer, F16
     (8, 2, 128, 3000, 12, 0, "f16", 1, 3000, 3),              # one layer, head_dim 128: separate launches
     (24, 4, 256, 50, 23, 0, "q4_0", 1, 64, 2),                # one layer, no whole chunk: merge, acceptance
