@@ -29,8 +29,10 @@
  *   - Host arrays passed in (parent, tokens) are read during the call only.
  *   - Every argument check runs on the host before anything is launched; on
  *     an error nothing is launched and no output is written.
- *   - The library keeps no mutable global state; calls from several threads
- *     on different streams are safe.
+ *   - Apart from tree_accept_noalloc's per-device acceptance array (see
+ *     there) and a per-device cache of the compute-unit count, the library
+ *     keeps no mutable global state; calls from several threads on
+ *     different streams with their own outputs and workspaces are safe.
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H
