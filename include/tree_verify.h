@@ -144,6 +144,8 @@ TV_API size_t tv_attn_workspace_bytes(const tv_attn_desc *d);
 #define TV_SPLIT_Q4_0 2  /* Q4_0 cache, one wave per SIMD, dequantisation interleaved with the MFMAs */
 #define TV_SPLIT_Q4_0_WS 3 /* Q4_0 cache, head_dim 256: two waves per SIMD, one running the MFMAs,
                               the other dequantising the next chunks */
+#define TV_SPLIT_F16_WS 4  /* F16 cache, head_dim 256: the same two roles, the other wave moving
+                              the next chunks into LDS (at most one shared tile) */
 
 /*
  * How tree_verify_attn would run `d` on a device with `n_cu` compute units

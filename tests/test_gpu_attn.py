@@ -163,8 +163,8 @@ def test_tile_layouts_27b_heads(n, layout, kv):
     groups of five (a group holds at most three tile slots per wave). The
     plan the library reports for this device is asserted first, so each case
     is known to run the tile layout and split kernel it is named for
-    (unmasked; every layout of the warp-specialised Q4_0 kernel is among
-    them)."""
+    (unmasked; every layout of the warp-specialised Q4_0 and F16 kernels is
+    among them)."""
     import tree_verify_attention_ddtree_amd as tv
     inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=16384, n_nodes=n, depth_cap=16,
                             seed=3000 + n, kv=kv)
@@ -174,7 +174,9 @@ def test_tile_layouts_27b_heads(n, layout, kv):
     plan = tv.tv_attn_plan(desc)
     assert (plan["own_tiles"], plan["shared_tiles"]) == layout[kv], plan
     assert plan["row_groups"] == (2 if n == 26 else 1) and plan["masked"] == 0, plan
-    want = {"f16": tv.TV_SPLIT_F16, "q4_0": tv.TV_SPLIT_Q4_0_WS if layout[kv][0] in (1, 2) else tv.TV_SPLIT_Q4_0}
+    own, sh = layout[kv]
+    want = {"f16": tv.TV_SPLIT_F16_WS if own in (1, 2) and sh <= 1 else tv.TV_SPLIT_F16,
+            "q4_0": tv.TV_SPLIT_Q4_0_WS if own in (1, 2) else tv.TV_SPLIT_Q4_0}
     assert plan["kernel"] == want[kv], plan
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err

@@ -211,17 +211,19 @@ def test_plan_query_layouts():
     """The 27B head layout (24 q / 4 kv heads) on 256 compute units, 256
     whole chunks per KV head: 8, 20 and 30 nodes give 3, 8 and 12 query
     tiles, which the Q4_0 kernels take as three shared tiles, two own tiles
-    per wave and three own tiles per wave, with one row group."""
+    per wave and three own tiles per wave, with one row group. F16 plans of
+    head_dim 256 with one or two own tiles and at most one shared tile take
+    the warp-specialised F16 kernel, the others the one-wave F16 kernel."""
     Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
     p = _plan(24, 4, 8, 256, Q, 16384)
     assert (p["own_tiles"], p["shared_tiles"], p["row_groups"], p["masked"]) == (0, 3, 1, 0)
     assert (p["splits"], p["chunks"], p["kernel"]) == (64, 256, tv.TV_SPLIT_Q4_0)
     p = _plan(24, 4, 8, 256, F, 16384)
-    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16)
+    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16_WS)
     for kv in (Q, F):
         p = _plan(24, 4, 20, 256, kv, 16384)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (2, 0, 1)
-        assert p["kernel"] == (tv.TV_SPLIT_Q4_0_WS if kv == Q else tv.TV_SPLIT_F16)
+        assert p["kernel"] == (tv.TV_SPLIT_Q4_0_WS if kv == Q else tv.TV_SPLIT_F16_WS)
         p = _plan(24, 4, 30, 256, kv, 16384)
         assert (p["own_tiles"], p["shared_tiles"], p["row_groups"]) == (3, 0, 1)
         # three own tiles per wave do not fit two waves per SIMD
@@ -233,12 +235,21 @@ def test_plan_query_layouts():
     assert p["kernel"] == tv.TV_SPLIT_Q4_0_WS
     p = _plan(24, 4, 23, 256, Q, 16384)
     assert (p["splits"], p["row_groups"]) == (64, 1)
-    # not where a group would leave the warp-specialised layouts (10 nodes:
-    # groups of two shared tiles) nor for F16 caches
+    # F16 likewise, on the warp-specialised F16 kernel; not where a group
+    # would leave the warp-specialised layouts (10 nodes: groups of two
+    # shared tiles)
+    p = _plan(24, 4, 23, 256, F, 8192)
+    assert (p["splits"], p["row_groups"], p["own_tiles"], p["shared_tiles"]) == (32, 2, 1, 1)
+    assert p["kernel"] == tv.TV_SPLIT_F16_WS
     p = _plan(24, 4, 10, 256, Q, 8192)
     assert (p["splits"], p["row_groups"], p["kernel"]) == (64, 1, tv.TV_SPLIT_Q4_0_WS)
-    p = _plan(24, 4, 23, 256, F, 8192)
-    assert (p["splits"], p["row_groups"]) == (64, 1)
+    p = _plan(24, 4, 23, 256, F, 16384)
+    assert (p["splits"], p["row_groups"], p["kernel"]) == (64, 1, tv.TV_SPLIT_F16_WS)
+    # F16 with two shared tiles (chain of 16 nodes), masked or head_dim 128:
+    # the one-wave F16 kernel
+    assert _plan(24, 4, 16, 256, F, 16384)["kernel"] == tv.TV_SPLIT_F16
+    assert _plan(24, 4, 23, 256, F, 8192 + 31)["kernel"] == tv.TV_SPLIT_F16
+    assert _plan(24, 4, 23, 128, F, 16384)["kernel"] == tv.TV_SPLIT_F16
     # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits,
     # on the warp-specialised kernel (head_dim 256)
     p = _plan(24, 4, 23, 256, Q, 131072)

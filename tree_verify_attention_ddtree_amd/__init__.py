@@ -73,6 +73,7 @@ TV_SPLIT_NONE = 0
 TV_SPLIT_F16 = 1
 TV_SPLIT_Q4_0 = 2
 TV_SPLIT_Q4_0_WS = 3
+TV_SPLIT_F16_WS = 4
 
 
 class TvStepPlanInfo(ctypes.Structure):

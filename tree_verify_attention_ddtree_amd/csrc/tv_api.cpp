@@ -121,12 +121,14 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     // row-group step below gives the rows two groups instead. The grid keeps
     // one workgroup per CU, each with twice the chunks and about half the
     // rows, and the merge reads half the partials (27B layer, Q4_0, 23
-    // nodes: 4K 25.3 -> 19.8 us, 8K 26.5 -> 23.5 us; no gain from 16K).
-    // Taken where both groups fit the warp-specialised Q4_0 kernel.
+    // nodes: 4K 25.3 -> 19.8 us, 8K 26.5 -> 23.5 us; no gain from 16K; F16
+    // at 8K: 25.5 -> 23.1 us). Taken where both groups fit a warp-specialised
+    // kernel (the one-wave F16 kernel gained nothing from it).
     RowPlan two;
-    const bool halve = d->kv_type == TV_KV_Q4_0 && out->rows.groups == 1 && out->rows.tiles >= 2 &&
+    const bool halve = out->rows.groups == 1 && out->rows.tiles >= 2 &&
                        rows_for_groups(out->rows.tiles, 2, three_shared, &two) &&
-                       ws_layout(d->head_dim, two.nown, two.nsh);
+                       (d->kv_type == TV_KV_Q4_0 ? ws_layout(d->head_dim, two.nown, two.nsh)
+                                                 : ws_layout_f16(d->head_dim, two.nown, two.nsh));
     auto splits = [&](int64_t n_chunks, bool may_halve) -> int {
         int64_t S = (n_cu + per - 1) / per;
         if (may_halve && halve && n_chunks <= 2 * S && (S + 1) / 2 * 2 * per <= n_cu) S = (S + 1) / 2;
@@ -202,6 +204,8 @@ int split_kernel_kind(const tv_attn_desc *d, const SplitPlan &p)
     if (p.S == 0) return TV_SPLIT_NONE;
     if (d->kv_type == TV_KV_Q4_0 && !p.mask && ws_layout(d->head_dim, p.rows.nown, p.rows.nsh))
         return TV_SPLIT_Q4_0_WS;
+    if (d->kv_type == TV_KV_F16 && !p.mask && ws_layout_f16(d->head_dim, p.rows.nown, p.rows.nsh))
+        return TV_SPLIT_F16_WS;
     return d->kv_type == TV_KV_Q4_0 ? TV_SPLIT_Q4_0 : TV_SPLIT_F16;
 }
 

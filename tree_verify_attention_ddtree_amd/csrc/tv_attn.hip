@@ -462,12 +462,18 @@ static split_fn pick_split(int D, int kv, int nown, int nsh, bool mask)
     return nullptr;
 }
 
-// The warp-specialised kernel takes unmasked Q4_0 plans whose tile layout it
-// has (head_dim 256; one or two own tiles per wave, at most two shared).
+// The warp-specialised kernels take unmasked plans whose tile layout they
+// have (head_dim 256; one or two own tiles per wave, at most two shared for
+// Q4_0 and one for F16).
 split_fn pick_ws(const tv_attn_desc *d, const SplitPlan &p)
 {
-    if (d->kv_type != TV_KV_Q4_0 || p.mask || !ws_layout(d->head_dim, p.rows.nown, p.rows.nsh)) return nullptr;
-    return pick_split_q4ws(d->head_dim, p.rows.nown, p.rows.nsh);
+    if (p.mask) return nullptr;
+    if (d->kv_type == TV_KV_Q4_0)
+        return ws_layout(d->head_dim, p.rows.nown, p.rows.nsh) ? pick_split_q4ws(d->head_dim, p.rows.nown, p.rows.nsh)
+                                                                : nullptr;
+    return ws_layout_f16(d->head_dim, p.rows.nown, p.rows.nsh)
+               ? pick_split_f16ws(d->head_dim, p.rows.nown, p.rows.nsh)
+               : nullptr;
 }
 
 void fill_split_args(const tv_attn_desc *d, const tv_attn_ptrs *p, const SplitPlan &plan, void *ws, SplitArgs *out)

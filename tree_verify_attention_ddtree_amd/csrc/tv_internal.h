@@ -63,6 +63,13 @@ inline bool ws_layout(int D, int nown, int nsh)
     return D == 256 && ((nown == 1 && nsh >= 0 && nsh <= 2) || (nown == 2 && nsh >= 0 && nsh <= 1));
 }
 
+// ... and of its F16 form (at most one shared tile: the load waves' raw F16
+// rows take the registers a second one would need).
+inline bool ws_layout_f16(int D, int nown, int nsh)
+{
+    return D == 256 && (nown == 1 || nown == 2) && nsh >= 0 && nsh <= 1;
+}
+
 // Sizes the host side needs from the kernels' layouts.
 constexpr size_t kAcceptWsBytes = 832;  // acceptance state: counters, per-row maxima
 constexpr int kSliceFloats = 16384;     // logits per acceptance workgroup (slice)

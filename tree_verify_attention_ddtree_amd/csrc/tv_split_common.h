@@ -496,5 +496,6 @@ split_fn pick_split_q4(int D, int nown, int nsh, bool mask);
 // The warp-specialised Q4_0 kernel (512 threads) for a tile layout, or null
 // when it has none (head_dim other than 256, other layouts).
 split_fn pick_split_q4ws(int D, int nown, int nsh);
+split_fn pick_split_f16ws(int D, int nown, int nsh);
 
 }  // namespace tv

@@ -85,6 +85,85 @@ struct FmStage {
     static constexpr int ELEMS = KELEMS + VELEMS;
 };
 
+// Loads and stage stores of the load waves for an F16 cache (head_dim 256):
+// no decoding, so a chunk moves from HBM into the fragment-order stage above
+// as it is, K by plain 16-byte stores and V through an 8 x 8 transposition
+// in registers. Lane mapping of load wave q:
+//   K: lane l holds key 16q + (l & 15), values 8 (l >> 4) .. + 7 of every
+//      block b (one 16-byte load per block, 64-byte spans of a row across
+//      the lanes l, l + 16, l + 32, l + 48) and stores the piece of block b
+//      at slot l of fragment 8q + b: each store instruction writes one whole
+//      1 KB fragment;
+//   V: lane l takes k-step kk = (l >> 2) & 1, row g = l & 3 and the
+//      8 values d0 = 64q + 8 (l >> 3) .. + 7, loads them for the eight keys
+//      of that slot (32kk + 4g + 0..3, 32kk + 16 + 4g + 0..3: one 16-byte
+//      load per key), transposes them with byte permutes into the eight
+//      slots (d0 & 15) + 0..7 of row g of fragment 2 (d0 >> 4) + kk. Eight
+//      lanes that store together (one d0, all kk and g) hit 128 distinct
+//      bytes of the banks (rows 272 bytes and fragments 1088 bytes apart).
+struct F16WsLoader {
+    const uint8_t *kbase;  // K cache of this KV head
+    const uint8_t *vbase;
+    int64_t tok_stride;
+    u32 chunk_bytes;  // 64 rows
+    u32 koff;         // K: byte offset of this lane's first piece inside a chunk
+    u32 voff;         // V: byte offset of this lane's first key and values
+    int lane;
+    int vdst;         // V: stage offset (halves) of this lane's first slot
+    u4v rk[8];        // K pieces, block b
+    u4v rv[8];        // V rows of the slot's eight keys, in the P^T key order
+
+    __device__ __forceinline__ void init_ws(const SplitArgs &a, const SplitPtrs &p, int gkv, int q, int ln)
+    {
+        kbase = p.k_cache + (int64_t)gkv * a.head_stride;
+        vbase = p.v_cache + (int64_t)gkv * a.head_stride;
+        tok_stride = a.tok_stride;
+        chunk_bytes = (u32)(kChunk * a.tok_stride);
+        lane = ln;
+        koff = (u32)((16 * q + (ln & 15)) * tok_stride) + 16u * (u32)(ln >> 4);
+        const int kk = (ln >> 2) & 1, g = ln & 3, d0 = 64 * q + 8 * (ln >> 3);
+        voff = (u32)((32 * kk + 4 * g) * tok_stride) + 2u * (u32)d0;
+        vdst = FmStage::KELEMS + (2 * (d0 >> 4) + kk) * FmStage::VFRAG + g * FmStage::VROW + 8 * (d0 & 15);
+    }
+
+    // A chunk past the split's end (valid false) gets an empty descriptor:
+    // its loads return zeros without touching memory (as Q4Loader's).
+    __device__ __forceinline__ void load_k_ws(int64_t chunk_row, bool valid)
+    {
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(kbase + chunk_row * tok_stride, valid ? chunk_bytes : 0u);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) rk[b] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 64 * b, 0);
+    }
+
+    __device__ __forceinline__ void load_v(int64_t chunk_row, bool valid)
+    {
+        const __amdgpu_buffer_rsrc_t r = chunk_rsrc(vbase + chunk_row * tok_stride, valid ? chunk_bytes : 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)(i * tok_stride), 0);
+            rv[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)((16 + i) * tok_stride), 0);
+        }
+    }
+
+    // the chunk into stage `stg` (K fragments 8q .. 8q + 7, V^T D-quarter q)
+    __device__ __forceinline__ void stage(_Float16 *stg, int q) const
+    {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) *(u4v *)(stg + (8 * q + b) * FmStage::KFRAG + 8 * lane) = rk[b];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // value d0 + e of the eight keys: half e & 1 of dword e >> 1
+            const u32 sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            u4v w;
+            w.x = __builtin_amdgcn_perm(rv[1][e >> 1], rv[0][e >> 1], sel);
+            w.y = __builtin_amdgcn_perm(rv[3][e >> 1], rv[2][e >> 1], sel);
+            w.z = __builtin_amdgcn_perm(rv[5][e >> 1], rv[4][e >> 1], sel);
+            w.w = __builtin_amdgcn_perm(rv[7][e >> 1], rv[6][e >> 1], sel);
+            *(u4v *)(stg + vdst + 8 * e) = w;
+        }
+    }
+};
+
 // LDS of a split workgroup (module-scope arrays; each kernel that uses them
 // gets its own): the two K / V^T stages (the query rows are staged there
 // first and the normalised output rows gathered there last) and the shared
@@ -101,15 +180,18 @@ static __shared__ __attribute__((aligned(16))) int ws_shflag[2][4];
 // workgroup of kWsThreads threads, in the arrays above, over the tensors `p`;
 // the partial state is stored with cache policy CPOL (the buffer stores' aux
 // bits: kCpolSc1 makes them coherent across the device's L2 caches). With `ticket` set, thread 0 also takes the
-// next ticket of a work queue into `next`.
-template <int NOWN, int NSH, int CPOL = 0>
+// next ticket of a work queue into `next`. KVT is the cache type: the load
+// waves dequantise a Q4_0 chunk or move an F16 chunk into the stage; the
+// math waves and the shared tiles see the same stage either way.
+template <int NOWN, int NSH, int CPOL = 0, int KVT = TV_KV_Q4_0>
 __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p, int split, int gkv, int rg, int RG,
                                          uint32_t *ticket, uint32_t &next)
 {
     constexpr int D = 256;
     using St = FmStage;
-    using L = Q4Loader<D, true>;  // its loads and decoding; the stage stores are this file's
-    using QS = QStage<D, TV_KV_Q4_0, NOWN, NSH, kWsThreads>;
+    // loads and decoding (Q4_0: the stage stores are this function's)
+    using L = std::conditional_t<KVT == TV_KV_Q4_0, Q4Loader<D, true>, F16WsLoader>;
+    using QS = QStage<D, KVT, NOWN, NSH, kWsThreads>;
     constexpr int NB = D / 32;     // 32-value blocks per row
     constexpr int NDT = D / 16;    // D tiles
     constexpr int NDQ = NDT / 4;   // D tiles of a quarter
@@ -318,27 +400,36 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
         // + (kappa >> 5), slot (8 vh + e) & 15.
         const int kq = lane & 15;
         const int ksto = (8 * q + 2 * (lane >> 4)) * St::KFRAG + 8 * kq;
-        const int vsto = St::KELEMS + (4 * ld0.vb + (kq >> 3)) * St::VFRAG + (kq & 3) * St::VROW + 64 * ld0.vh +
-                         4 * ((kq >> 2) & 1);
+        const int vsto = [&]() {
+            if constexpr (KVT == TV_KV_Q4_0)
+                return St::KELEMS + (4 * ld0.vb + (kq >> 3)) * St::VFRAG + (kq & 3) * St::VROW + 64 * ld0.vh +
+                       4 * ((kq >> 2) & 1);
+            else
+                return 0;
+        }();
         auto deq = [&](const L &ld, _Float16 *stg) {
+            if constexpr (KVT == TV_KV_F16) {
+                ld.stage(stg, q);
+            } else {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                int b, g;
-                const h8 o = ld.k_values(j, magic, b, g);
-                *(h8 *)(stg + ksto + (j >> 2) * St::KFRAG + 128 * (j & 3)) = o;
-            }
+                for (int j = 0; j < NB; ++j) {
+                    int b, g;
+                    const h8 o = ld.k_values(j, magic, b, g);
+                    *(h8 *)(stg + ksto + (j >> 2) * St::KFRAG + 128 * (j & 3)) = o;
+                }
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                h2 vals[2][4];
-                ld.v_values(pc, magic, vals);
-                // element e = 4 (pc >> 1) + 2 (pc & 1) + {0, 1, 16, 17}[t]
-                const int de = 4 * (pc >> 1) + 2 * (pc & 1);
+                for (int pc = 0; pc < 4; ++pc) {
+                    h2 vals[2][4];
+                    ld.v_values(pc, magic, vals);
+                    // element e = 4 (pc >> 1) + 2 (pc & 1) + {0, 1, 16, 17}[t]
+                    const int de = 4 * (pc >> 1) + 2 * (pc & 1);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    h4 w4;
-                    w4.s01 = vals[0][t];
-                    w4.s23 = vals[1][t];
-                    *(h4 *)(stg + vsto + (t >> 1) * 2 * St::VFRAG + 8 * (de + (t & 1))) = w4;
+                    for (int t = 0; t < 4; ++t) {
+                        h4 w4;
+                        w4.s01 = vals[0][t];
+                        w4.s23 = vals[1][t];
+                        *(h4 *)(stg + vsto + (t >> 1) * 2 * St::VFRAG + 8 * (de + (t & 1))) = w4;
+                    }
                 }
             }
         };
