@@ -643,9 +643,10 @@ def budget_sweep(args):
     and 128K context, Q4_0 and F16, with the 27B head layout (24 q / 4 kv
     heads, head_dim 256): random draft trees of depth <= 16, plus chains of
     the same size. The cache rotates over copies spanning >= 1.1 GB so that
-    every launch streams it from HBM. Each point: the average of 200 launches
-    after 50, the KV bandwidth, the MFMA rate and the fraction of the binding
-    roofline (HBM below 312 FLOP per KV byte, MFMA above)."""
+    every launch streams it from HBM. Each point: the median of six runs of
+    40 launches (each led by 40 untimed ones) after 50, the KV bandwidth, the
+    MFMA rate and the fraction of the binding roofline (HBM below 312 FLOP
+    per KV byte, MFMA above)."""
     import torch
 
     import synth
@@ -685,7 +686,7 @@ def budget_sweep(args):
                         tv.tree_verify_attn(desc, kc, vc, q, kt, vt, out, ws, wsb, stream)
 
                     timed(torch, stream, launch, 50)
-                    us = timed(torch, stream, launch, 200) * 1e3
+                    us = timed_median(torch, stream, launch, 240) * 1e3
                     rec = attn_record(us, layer_bytes, 4.0 * Hq * n * T * D)
                     row = dict(kv=kv, n_ctx=T, n=n, tree=shape, us=us, kv_gbps=rec["kv_gbps"], tflops=rec["tflops"],
                                bound=rec["bound"], frac=rec["frac"])

@@ -152,19 +152,21 @@ def test_tile_layouts(Hq, Hkv, n, D, kv):
 
 
 @pytest.mark.parametrize("kv", ["q4_0", "f16"])
-@pytest.mark.parametrize("n,layout", [(8, {"q4_0": (0, 3), "f16": (1, 0)}), (20, {"q4_0": (2, 0), "f16": (2, 0)}),
+@pytest.mark.parametrize("n,layout", [(8, {"q4_0": (1, 0), "f16": (1, 0)}), (20, {"q4_0": (2, 0), "f16": (2, 0)}),
                                       (30, {"q4_0": (3, 0), "f16": (3, 0)}), (23, {"q4_0": (2, 1), "f16": (2, 1)}),
                                       (10, {"q4_0": (1, 0), "f16": (1, 0)}), (11, {"q4_0": (1, 1), "f16": (1, 1)}),
-                                      (16, {"q4_0": (1, 2), "f16": (1, 2)}), (26, {"q4_0": (1, 1), "f16": (1, 1)})])
+                                      (16, {"q4_0": (1, 2), "f16": (2, 0)}), (26, {"q4_0": (1, 1), "f16": (1, 1)}),
+                                      (2, {"q4_0": (0, 1), "f16": (1, 0)})])
 def test_tile_layouts_27b_heads(n, layout, kv):
     """The 27B head layout (24 q / 4 kv heads) over 256 whole chunks per KV
-    head: 8, 20, 30, 23, 10, 11 and 16 nodes make 3, 8, 12, 9, 4, 5 and 6
-    query tiles in one row group; 26 nodes make 10 tiles, cut into two row
-    groups of five (a group holds at most three tile slots per wave). The
-    plan the library reports for this device is asserted first, so each case
-    is known to run the tile layout and split kernel it is named for
-    (unmasked; every layout of the warp-specialised Q4_0 and F16 kernels is
-    among them)."""
+    head: 8, 20, 30, 23, 10, 11, 16 and 2 nodes make 3, 8, 12, 9, 4, 5, 6 and
+    1 query tiles in one row group; 26 nodes make 10 tiles, cut into two row
+    groups of five (a group holds at most three tile slots per wave). Small
+    layouts the warp-specialised kernels lack run on one they have with idle
+    tile slots (Q4_0: three tiles; F16: up to eight). The plan the library
+    reports for this device is asserted first, so each case is known to run
+    the tile layout and split kernel it is named for (unmasked; every layout
+    of the warp-specialised Q4_0 and F16 kernels is among them)."""
     import tree_verify_attention_ddtree_amd as tv
     inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=16384, n_nodes=n, depth_cap=16,
                             seed=3000 + n, kv=kv)
@@ -178,6 +180,26 @@ def test_tile_layouts_27b_heads(n, layout, kv):
     want = {"f16": tv.TV_SPLIT_F16_WS if own in (1, 2) and sh <= 1 else tv.TV_SPLIT_F16,
             "q4_0": tv.TV_SPLIT_Q4_0_WS if own in (1, 2) else tv.TV_SPLIT_Q4_0}
     assert plan["kernel"] == want[kv], plan
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kv,n,layout", [("q4_0", 8, (0, 3)), ("f16", 16, (1, 2)), ("q4_0", 16, (1, 2))])
+def test_masked_layouts_one_wave_kernels(kv, n, layout):
+    """A ragged end (16384 + 31 rows: short splits, so the masked kernels):
+    the layouts the warp-specialised kernels would otherwise take over (three
+    shared Q4_0 tiles; one own and two shared F16 tiles) on the one-wave
+    masked kernels, against the oracle."""
+    import tree_verify_attention_ddtree_amd as tv
+    T = 16384 + 31
+    inp = synth.attn_inputs(n_q_heads=24, n_kv_heads=4, head_dim=256, n_ctx=T, n_nodes=n, depth_cap=16,
+                            seed=3100 + n, kv=kv)
+    kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+    row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
+    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, T, 0, inp["scale"], row, row * T)
+    plan = tv.tv_attn_plan(desc)
+    assert (plan["own_tiles"], plan["shared_tiles"], plan["masked"]) == layout + (1,), plan
+    assert plan["kernel"] == (tv.TV_SPLIT_Q4_0 if kv == "q4_0" else tv.TV_SPLIT_F16), plan
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
 

@@ -210,14 +210,22 @@ def _plan(Hq, Hkv, n, D, kv, n_ctx, window=0, window_mode=0, n_cu=256):
 def test_plan_query_layouts():
     """The 27B head layout (24 q / 4 kv heads) on 256 compute units, 256
     whole chunks per KV head: 8, 20 and 30 nodes give 3, 8 and 12 query
-    tiles, which the Q4_0 kernels take as three shared tiles, two own tiles
-    per wave and three own tiles per wave, with one row group. F16 plans of
-    head_dim 256 with one or two own tiles and at most one shared tile take
-    the warp-specialised F16 kernel, the others the one-wave F16 kernel."""
+    tiles, which the Q4_0 kernels take as one own tile per wave (three
+    shared tiles moved onto the warp-specialised kernel, one slot idle), two
+    own tiles per wave and three own tiles per wave, with one row group. F16
+    plans of head_dim 256 up to 8 tiles take the warp-specialised F16 kernel
+    with one or two own tiles per wave, and with at most one shared tile
+    above; the others the one-wave F16 kernel."""
     Q, F = tv.TV_KV_Q4_0, tv.TV_KV_F16
     p = _plan(24, 4, 8, 256, Q, 16384)
-    assert (p["own_tiles"], p["shared_tiles"], p["row_groups"], p["masked"]) == (0, 3, 1, 0)
-    assert (p["splits"], p["chunks"], p["kernel"]) == (64, 256, tv.TV_SPLIT_Q4_0)
+    assert (p["own_tiles"], p["shared_tiles"], p["row_groups"], p["masked"]) == (1, 0, 1, 0)
+    assert (p["splits"], p["chunks"], p["kernel"]) == (64, 256, tv.TV_SPLIT_Q4_0_WS)
+    # ... but a masked plan keeps the three shared tiles (one-wave kernel)
+    p = _plan(24, 4, 8, 256, Q, 16384 + 31)
+    assert (p["own_tiles"], p["shared_tiles"], p["masked"], p["kernel"]) == (0, 3, 1, tv.TV_SPLIT_Q4_0)
+    # one or two Q4_0 tiles stay all-shared on the one-wave kernel
+    p = _plan(24, 4, 2, 256, Q, 16384)
+    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (0, 1, tv.TV_SPLIT_Q4_0)
     p = _plan(24, 4, 8, 256, F, 16384)
     assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16_WS)
     for kv in (Q, F):
@@ -245,9 +253,13 @@ def test_plan_query_layouts():
     assert (p["splits"], p["row_groups"], p["kernel"]) == (64, 1, tv.TV_SPLIT_Q4_0_WS)
     p = _plan(24, 4, 23, 256, F, 16384)
     assert (p["splits"], p["row_groups"], p["kernel"]) == (64, 1, tv.TV_SPLIT_F16_WS)
-    # F16 with two shared tiles (chain of 16 nodes), masked or head_dim 128:
-    # the one-wave F16 kernel
-    assert _plan(24, 4, 16, 256, F, 16384)["kernel"] == tv.TV_SPLIT_F16
+    # F16 with six tiles (16 nodes): two own tiles per wave, two slots idle,
+    # instead of (1, 2); one or two tiles: one own tile per wave
+    p = _plan(24, 4, 16, 256, F, 16384)
+    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (2, 0, tv.TV_SPLIT_F16_WS)
+    p = _plan(24, 4, 2, 256, F, 16384)
+    assert (p["own_tiles"], p["shared_tiles"], p["kernel"]) == (1, 0, tv.TV_SPLIT_F16_WS)
+    # masked or head_dim 128: the one-wave F16 kernel
     assert _plan(24, 4, 23, 256, F, 8192 + 31)["kernel"] == tv.TV_SPLIT_F16
     assert _plan(24, 4, 23, 128, F, 16384)["kernel"] == tv.TV_SPLIT_F16
     # budget 22 at 128K: two own tiles per wave and a shared one, 64 splits,
