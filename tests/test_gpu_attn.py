@@ -288,19 +288,27 @@ def test_budget_zero_decode():
     assert err <= TOL, err
 
 
-def test_token_major_strided_cache():
-    """Cache laid out [token][head][row] (ggml-like) instead of head-major."""
+@pytest.mark.parametrize("kv,n_ctx", [("q4_0", 1500), ("f16", 1500), ("q4_0", 1536), ("f16", 1536)])
+def test_token_major_strided_cache(kv, n_ctx):
+    """Cache laid out [token][head][row] (ggml-like) instead of head-major:
+    a ragged end (the masked one-wave kernels) and whole chunks (the
+    warp-specialised kernels)."""
     import torch
 
     import tree_verify_attention_ddtree_amd as tv
-    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=1500))
+    inp = synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=n_ctx), kv=kv)
     t = {}
     for k in ("k_cache", "v_cache"):
         tm = np.ascontiguousarray(inp[k].transpose(1, 0, 2))  # [T][H][row]
         t[k] = torch.from_numpy(tm).cuda()
     for k in ("q", "k_tree", "v_tree"):
         t[k] = torch.from_numpy(inp[k]).cuda()
-    row = inp["k_cache"].shape[2]
+    row = inp["k_cache"].shape[2] * inp["k_cache"].itemsize
+    kvt = tv.TV_KV_Q4_0 if kv == "q4_0" else tv.TV_KV_F16
+    desc, _par = tv.make_desc(inp["parent"], 24, 4, 256, kvt, n_ctx, 0, inp["scale"], row * 4, row)
+    plan = tv.tv_attn_plan(desc)
+    ws_kind = tv.TV_SPLIT_Q4_0_WS if kv == "q4_0" else tv.TV_SPLIT_F16_WS
+    assert (plan["kernel"] == ws_kind) == (n_ctx % 64 == 0), plan
     got = gpu_attn(inp, tensors=t, strides=(row * inp["n_kv_heads"], row))
     err = rownorm_err(got.astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
