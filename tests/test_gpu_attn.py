@@ -487,3 +487,41 @@ def test_remainder_rows_left_to_merge_kernel(kv, mode):
         inp = dict(inp, window=16415, window_mode=1)
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
+
+
+def _random_shapes(k, seed):
+    """k seeded layer shapes across the descriptor's range: head dims, head
+    counts and GQA groups, tree sizes 1..64, contexts from a few rows to a few
+    thousand (whole chunks or ragged), windows of either mode, both cache
+    types; sized so the oracle takes at most a few seconds each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < k:
+        D = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.integers(1, 9))
+        n = int(rng.integers(1, 65))
+        T = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 6000)), 64 * int(rng.integers(1, 90))]))
+        W = int(rng.choice([0, 0, int(rng.integers(1, 3000))]))
+        wm = int(rng.integers(0, 2)) if W else 0
+        kv = str(rng.choice(["q4_0", "f16"]))
+        if G * Hkv * n * T * D > 3e9:
+            continue
+        out.append((G * Hkv, Hkv, D, T, n, W, wm, kv, int(rng.integers(1 << 30))))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(96, 20261203)
+
+
+@pytest.mark.parametrize("shape", RANDOM_SHAPES,
+                         ids=[f"{s[0]}x{s[1]}x{s[2]}-T{s[3]}-n{s[4]}-W{s[5]}m{s[6]}-{s[7]}" for s in RANDOM_SHAPES])
+def test_random_shapes(shape):
+    """Seeded random shapes against the oracle: whatever split kernel, tile
+    layout, row grouping, masking and merge path the planner picks for each."""
+    Hq, Hkv, D, T, n, W, wm, kv, seed = shape
+    inp = synth.attn_inputs(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_ctx=T, n_nodes=n, depth_cap=16, seed=seed,
+                            kv=kv, window=W)
+    inp["window_mode"] = wm
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
