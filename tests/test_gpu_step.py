@@ -190,3 +190,54 @@ def test_full_step_16_layers_one_launch():
         del tens
     err = rownorm_err(got[0][15].astype(np.float64), oracle.attn(inps[15]))
     assert err <= TOL, err
+
+
+def _random_step_shapes(k, seed):
+    """k seeded step shapes: layer counts 1..4, head layouts, tree sizes,
+    contexts (whole chunks or ragged), windows, both cache types, vocabularies
+    from 64 logits to two 16384-logit slices and a bit; every third shape is
+    one the work-queue kernel takes, and every third one layer of head_dim
+    256 (two launches)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < k:
+        D = int(rng.choice([128, 256, 256]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.integers(1, 8))
+        n = int(rng.integers(1, 41))
+        T = int(rng.choice([int(rng.integers(1, 3000)), 64 * int(rng.integers(1, 48))]))
+        W = int(rng.choice([0, 0, int(rng.integers(1, 2500))]))
+        kv = str(rng.choice(["q4_0", "q4_0", "f16"]))
+        L = int(rng.integers(1, 5))
+        # (at least as many tokens as a node can have children: the draft
+        # tokens of siblings are distinct)
+        vocab = int(rng.choice([64, int(rng.integers(65, 5000)), int(rng.integers(16000, 40000))]))
+        if len(out) % 3 == 0:
+            # a shape for the work-queue kernel: several layers of head_dim
+            # 256 over enough whole chunks of a Q4_0 cache, no window
+            D, kv, W, L = 256, "q4_0", 0, int(rng.integers(2, 5))
+            T = 64 * int(rng.integers(64, 160))
+        elif len(out) % 3 == 1:
+            # one layer of head_dim 256: the two-launch form
+            D, L = 256, 1
+        if L * G * Hkv * n * T * D > 2e9:
+            continue
+        out.append((G * Hkv, Hkv, D, T, n, W, kv, L, vocab, int(rng.integers(1 << 20))))
+    return out
+
+
+RANDOM_STEPS = _random_step_shapes(24, 20261204)
+
+
+@pytest.mark.parametrize("shape", RANDOM_STEPS,
+                         ids=[f"{s[0]}x{s[1]}x{s[2]}-T{s[3]}-n{s[4]}-W{s[5]}-{s[6]}-L{s[7]}-V{s[8]}" for s in RANDOM_STEPS])
+def test_random_step_shapes(shape):
+    """Seeded random steps: whatever launch form the plan takes (work queue,
+    two launches, separate launches) equals the separate calls, the
+    acceptance the oracle's, and every layer the oracle within the bound."""
+    Hq, Hkv, D, T, n, W, kv, L, vocab, seed = shape
+    w = dict(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, n_ctx=T, n_nodes=n, depth_cap=16, kv=kv, window=W)
+    inps = _same_tree([synth.attn_inputs(**dict(w, seed=seed + 7 * l)) for l in range(L)])
+    for x in inps:
+        x["window"] = W
+    check_step(inps, vocab, seed + 1, oracle_layers=range(L))
