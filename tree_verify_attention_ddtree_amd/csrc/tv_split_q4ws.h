@@ -1,6 +1,8 @@
-// Warp-specialised split workgroup for Q4_0 caches with head_dim 256 (gfx950),
-// internal header of libtv.so: the body shared by split_q4ws_kernel and the
-// work-queue step kernel.
+// Warp-specialised split workgroup for Q4_0 and F16 caches with head_dim 256
+// (gfx950), internal header of libtv.so: the body shared by
+// split_q4ws_kernel, split_f16ws_kernel and the work-queue step kernel. The
+// notes below describe the Q4_0 form; the F16 form differs only in what the
+// load waves do to a chunk (F16WsLoader: no decoding).
 //
 // Method: every node of a DDTree draft tree attends to the committed Q4_0 KV
 // cache in one verify pass ("Luce DFlash: 単一RTX 3090で最大2倍のスループット
