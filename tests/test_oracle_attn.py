@@ -254,3 +254,20 @@ def test_rejects_bad_trees():
     assert oracle.check_tree(np.array([-1, 1], np.int32)) != 0
     assert oracle.check_tree(np.array([-1, 0, 3, 1], np.int32)) != 0
     assert oracle.check_tree(np.array([-1, -1], np.int32)) != 0
+
+
+@pytest.mark.parametrize("kv", ["q4_0", "f16"])
+def test_cache_row_order_does_not_matter(kv):
+    """Attention is a sum over keys: the same cache rows (K with its V) in any
+    order give the same output (up to summation order), and exchanging the V
+    rows of two keys alone changes it (a K/V row mismatch would not)."""
+    w = dict(n_q_heads=6, n_kv_heads=2, head_dim=64, n_ctx=300, n_nodes=9, depth_cap=4, seed=515, kv=kv)
+    inp = synth.attn_inputs(**w)
+    base = oracle.attn(inp)
+    perm = np.random.default_rng(7).permutation(300)
+    shuf = dict(inp, k_cache=np.ascontiguousarray(inp["k_cache"][:, perm]),
+                v_cache=np.ascontiguousarray(inp["v_cache"][:, perm]))
+    assert rownorm_err(oracle.attn(shuf), base) <= TOL
+    swapped_v = inp["v_cache"].copy()
+    swapped_v[:, [3, 200]] = swapped_v[:, [200, 3]]
+    assert rownorm_err(oracle.attn(dict(inp, v_cache=swapped_v)), base) > 1e-6
