@@ -121,7 +121,8 @@ def _same_tree(inps):
 # launches the plan must make). The single-launch shapes cover
 # every tile layout of the work-queue kernel: M = 6 n query rows per KV head
 # in T = ceil(M / 16) tiles; T = 9 -> (2, 1), 4 -> (1, 0), 5 -> (1, 1),
-# 6 -> (1, 2), 8 -> (2, 0).
+# 6 -> (2, 0) (two idle slots), 8 -> (2, 0); 12 tiles in two row groups
+# (a 2048-row window) -> (1, 2).
 SHAPES = [
     (24, 4, 256, 4096, 23, 0, "q4_0", 3, 152000, True),
     (24, 4, 256, 2048 + 64 * 5, 10, 0, "q4_0", 2, 16385, True),      # last acceptance slice of one logit
@@ -130,6 +131,7 @@ SHAPES = [
     (24, 4, 256, 4096, 20, 0, "q4_0", 2, 1000, True),
     (24, 4, 256, 33000, 23, 0, "q4_0", 2, 5000, True),        # 40 tail rows left to the merge
     (24, 4, 256, 8192, 23, 2048, "q4_0", 2, 777, True),       # 2048-row window: two row groups
+    (24, 4, 256, 8192, 32, 2048, "q4_0", 2, 777, True),       # the same with 32 nodes: (1, 2) per group
     (24, 4, 256, 4096 + 37, 23, 0, "q4_0", 2, 5000, None),    # ragged end: masked split kernel
     (24, 4, 256, 6000, 30, 0, "q4_0", 2, 1000, None),         # three own tiles per wave
     (24, 4, 256, 50, 23, 0, "q4_0", 2, 64, False),            # no whole chunk: merge only

@@ -267,8 +267,13 @@ def test_plan_query_layouts():
     p = _plan(24, 4, 23, 256, Q, 131072)
     assert (p["own_tiles"], p["shared_tiles"], p["splits"], p["chunks"]) == (2, 1, 64, 2048)
     assert p["kernel"] == tv.TV_SPLIT_Q4_0_WS
-    # the chain-16 (six tiles: one own, two shared) too; head_dim 128 does not
-    assert _plan(24, 4, 16, 256, Q, 131072)["kernel"] == tv.TV_SPLIT_Q4_0_WS
+    # the chain-16 (six tiles: two own tiles per wave, two slots idle) too;
+    # head_dim 128 does not
+    p16 = _plan(24, 4, 16, 256, Q, 131072)
+    assert (p16["own_tiles"], p16["shared_tiles"], p16["kernel"]) == (2, 0, tv.TV_SPLIT_Q4_0_WS)
+    # twelve tiles in the two row groups of a 2048-row window: (1, 2)
+    p12 = _plan(24, 4, 32, 256, Q, 8192, window=2048)
+    assert (p12["own_tiles"], p12["shared_tiles"], p12["row_groups"], p12["kernel"]) == (1, 2, 2, tv.TV_SPLIT_Q4_0_WS)
     assert _plan(24, 4, 23, 128, Q, 131072)["kernel"] == tv.TV_SPLIT_Q4_0
     assert p["workspace_bytes"] == 64 * 23 * 24 * (2 * 256 + 4)
     # a 2048-row window: 32 chunks cap the splits, the rows are cut in two groups

@@ -197,9 +197,12 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
     //   all-shared or (1, 2) layouts of the one-wave kernel (128K: 4 nodes
     //   122 -> 97 us, 16 nodes 135 -> 105; 8K: 4 nodes 27.0 -> 16.2);
     //   Q4_0, three tiles: one own tile per wave instead of three shared (8
-    //   nodes at 128K: 67.4 -> 61.3 us). One or two Q4_0 tiles stay on the
-    //   one-wave kernel, which measured faster there (1 node: 55.8 against
-    //   61.7 us).
+    //   nodes at 128K: 67.4 -> 61.3 us); six tiles: two own tiles per wave
+    //   instead of one own and two shared, which takes the two shared tiles
+    //   off the load waves (16 nodes at 128K: 83.9 -> 81.8 us, at 32K 31.3
+    //   -> 30.5; five tiles measured slower that way). One or two Q4_0 tiles
+    //   stay on the one-wave kernel, which measured faster there (1 node:
+    //   55.8 against 61.7 us).
     RowPlan &r = out->rows;
     if (!out->mask && r.groups == 1) {
         if (d->kv_type == TV_KV_F16 && r.tiles <= 8 && !ws_layout_f16(d->head_dim, r.nown, r.nsh) &&
@@ -208,6 +211,10 @@ int plan_attn(const tv_attn_desc *d, int n_cu, SplitPlan *out)
             r.nsh = 0;
         } else if (d->kv_type == TV_KV_Q4_0 && r.tiles == 3 && r.nown == 0 && ws_layout(d->head_dim, 1, 0)) {
             r.nown = 1;
+            r.nsh = 0;
+        } else if (d->kv_type == TV_KV_Q4_0 && r.tiles == 6 && r.nown == 1 && r.nsh == 2 &&
+                   ws_layout(d->head_dim, 2, 0)) {
+            r.nown = 2;
             r.nsh = 0;
         }
     }
