@@ -131,3 +131,22 @@ def test_stream_probe_reads_every_byte():
     assert int(got) == int(np.bitwise_xor.reduce(buf_np))
     tv.tv_stream_probe(buf, tv.TV_PROBE_Q4_0_DECODE, chk)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_trees_and_tied_logits(seed):
+    """Seeded random trees (1..64 nodes, random depth caps), vocabularies
+    from 1 to 40000 (slice edges included), logits drawn from a few values so
+    that argmax ties are common, draft tokens that often match the parent's
+    argmax (long accepted paths and competing equal-length paths), against
+    the oracle bit for bit."""
+    rng = np.random.default_rng(9000 + seed)
+    n = int(rng.integers(1, 65))
+    parent = synth.draft_tree(rng, n, int(rng.integers(1, 17)))
+    vocab = int(rng.choice([1, 2, int(rng.integers(3, 3000)), 16384, 16385, int(rng.integers(3000, 40000))]))
+    levels = rng.integers(1, 5)
+    logits = rng.integers(0, levels + 1, size=(n, vocab)).astype(np.float32) * np.float32(0.5)
+    am = logits.argmax(axis=1)  # first maximum: the smallest index on ties
+    tok = np.where(rng.random(n) < 0.7, am[np.maximum(parent, 0)], rng.integers(0, vocab, size=n)).astype(np.int32)
+    tok[0] = -1
+    check(logits, parent, tok)
