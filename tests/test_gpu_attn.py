@@ -525,3 +525,35 @@ def test_random_shapes(shape):
     inp["window_mode"] = wm
     err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
     assert err <= TOL, err
+
+
+def test_two_streams_own_workspaces():
+    """Calls on two streams at once, each with its own inputs, outputs and
+    workspace (the header's threading note): both match the oracle."""
+    import torch
+
+    import tree_verify_attention_ddtree_amd as tv
+    from gpu_util import to_dev
+    inps = [synth.attn_inputs(**dict(synth.WORKLOADS["27b"], n_ctx=4096 + 64 * k, seed=6100 + k)) for k in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    keep = []
+    for inp, st in zip(inps, streams):
+        t = to_dev(inp, "cuda")
+        ts, hs = tv.cache_strides(t["k_cache"], tv.TV_KV_Q4_0)
+        desc, par = tv.make_desc(inp["parent"], 24, 4, 256, tv.TV_KV_Q4_0, inp["k_cache"].shape[1], 0, inp["scale"],
+                                 ts, hs)
+        wsb = tv.tv_attn_workspace_bytes(desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        out = torch.full((23, 24, 256), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        keep.append((t, desc, par, ws))
+        outs.append(out)
+    for (t, desc, par, ws), out, st in zip(keep, outs, streams):
+        for _ in range(5):
+            tv.tree_verify_attn(desc, t["k_cache"], t["v_cache"], t["q"], t["k_tree"], t["v_tree"], out, ws,
+                                ws.numel(), st)
+    torch.cuda.synchronize()
+    for inp, out in zip(inps, outs):
+        err = rownorm_err(out.cpu().numpy().astype(np.float64), oracle.attn(inp))
+        assert err <= TOL, err
