@@ -12,9 +12,10 @@ the 256 MB Infinity Cache cannot hold it between steps.
 Prints one JSON line (progress goes to stderr). `value` is verify steps per
 second. Extra fields give the effective KV bandwidth, the roofline of the
 attention launch, the stream probes on the same caches, one record per
-workload (tiny, 27B-shaped at 8K, 128K tree and chain, the 2048-token window
-uniform and per position, the 16-layer step at 32K over its 64 seeded trees)
-and the CPU oracle's speed on bounded samples of each.
+workload (tiny, 27B-shaped at 8K, 128K tree and chain, 128K with an F16
+cache, the 2048-token window uniform and per position, the 16-layer step at
+32K over its 64 seeded trees) and the CPU oracle's speed on bounded samples
+of each.
 
 The per-workload measurements run before the headline's warm-up and timed
 steps, so that the headline is taken on a device at its steady clocks.
@@ -259,7 +260,8 @@ def stream_probes(torch, tv, stream, caches, kv_bytes):
         out[name] = {"us": ms * 1e3, "gbps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     out["bytes_per_call"] = kv_bytes
     out["note"] = ("K and V caches of the 128K layer (rotated copies), two launches of 2048 workgroups x 256 "
-                   "threads per call; q4_0_decode unpacks every code byte into fp16 (code - 8) * scale")
+                   "threads per call, each workgroup one contiguous range read with streaming loads; "
+                   "q4_0_decode unpacks every code byte into fp16 (code - 8) * scale")
     log(f"stream probes: read {out['read']['gbps']:.0f} GB/s, q4_0 decode {out['q4_0_decode']['gbps']:.0f} GB/s")
     return out
 
@@ -481,6 +483,9 @@ def main():
         cfg["window_61k_w2048_per_position"] = layer_config(torch, tv, dev, stream, "61K per-position window 2048",
                                                             24, 4, 256, 61440, 2048, "q4_0", p61, window_mode=1,
                                                             seed=42)
+        # the headline layer with an F16 cache (3.6x the KV bytes of Q4_0)
+        cfg["long_128k_f16"] = layer_config(torch, tv, dev, stream, "128K f16", Hq, Hkv, D, T, 0, "f16", parent,
+                                            seed=31)
         timed(torch, stream, attn, 50)
         ms_tree = timed_median(torch, stream, attn, 500)
         cfg["long_128k_tree"] = attn_record(ms_tree * 1e3, kv_bytes, flops)

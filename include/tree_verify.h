@@ -419,9 +419,11 @@ TV_API int tree_verify_step(const tv_attn_desc *d, int32_t n_layers, const tv_at
  * kernels' own. TV_PROBE_READ only reads; TV_PROBE_Q4_0_DECODE also turns
  * every 4-bit code into fp16 (code - 8) * scale, with the instruction mix
  * the split kernels use (the scale is a constant; block scales are not
- * parsed). n_checksums workgroups (1 .. 2^20) each write one checksum word to
- * the device array `checksums` (4-byte aligned), whose values only keep the
- * reads from being optimised away. Asynchronous on `stream`.
+ * parsed). n_checksums workgroups (1 .. 2^20) each read one of
+ * n_checksums near-equal contiguous ranges with streaming loads and write one
+ * checksum word to the device array `checksums` (4-byte aligned), whose
+ * values only keep the reads from being optimised away. Asynchronous on
+ * `stream`.
  * Returns TV_OK or a TV_E_* code (nothing is launched on error).
  */
 TV_API int tv_stream_probe(const void *buf, uint64_t bytes, int32_t kind, uint32_t *checksums,

@@ -131,6 +131,12 @@ def test_stream_probe_reads_every_byte():
     assert int(got) == int(np.bitwise_xor.reduce(buf_np))
     tv.tv_stream_probe(buf, tv.TV_PROBE_Q4_0_DECODE, chk)
     torch.cuda.synchronize()
+    # fewer 16-byte pieces than workgroups: the first ten read one each
+    small = torch.from_numpy(buf_np[:40].view(np.int32)).cuda()
+    tv.tv_stream_probe(small, tv.TV_PROBE_READ, chk)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(chk.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(buf_np[:40]))
 
 
 @pytest.mark.parametrize("seed", range(40))

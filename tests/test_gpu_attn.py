@@ -88,6 +88,18 @@ def test_long_128k_all_rows(tree):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("tree", ["budget22", "chain16"])
+def test_long_128k_f16_all_rows(tree):
+    """The same layer with an F16 cache (the warp-specialised F16 kernel at
+    64 splits: two own tiles and one shared per wave for the budget-22 tree,
+    two own for the chain), on every output row."""
+    w = dict(synth.WORKLOADS["long"])
+    parent = synth.chain_tree(16) if tree == "chain16" else None
+    inp = synth.attn_inputs(**w, parent=parent, kv="f16")
+    err = rownorm_err(gpu_attn(inp).astype(np.float64), oracle.attn(inp))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("layer,tree", [(0, 0), (0, 1), (15, 0), (15, 1)])
 def test_full_step_layer_tree_all_rows(layer, tree):
     """Layers 0 and 15 of the 16-layer verify step at 32768 rows, for trees 0
