@@ -147,11 +147,22 @@ struct F16WsLoader {
         }
     }
 
-    // the chunk into stage `stg` (K fragments 8q .. 8q + 7, V^T D-quarter q)
+    // the chunk into stage `stg` (K fragments 8q .. 8q + 7, V^T D-quarter q),
+    // K and V halves apart
     __device__ __forceinline__ void stage(_Float16 *stg, int q) const
+    {
+        stage_k(stg, q);
+        stage_v(stg);
+    }
+
+    __device__ __forceinline__ void stage_k(_Float16 *stg, int q) const
     {
 #pragma unroll
         for (int b = 0; b < 8; ++b) *(u4v *)(stg + (8 * q + b) * FmStage::KFRAG + 8 * lane) = rk[b];
+    }
+
+    __device__ __forceinline__ void stage_v(_Float16 *stg) const
+    {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             // value d0 + e of the eight keys: half e & 1 of dword e >> 1
@@ -514,6 +525,16 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
         auto body = [&](auto stc, int i) {
             constexpr int st = decltype(stc)::value;
             __syncthreads();
+            if constexpr (KVT == TV_KV_F16) {
+                // F16: the K half of stage st ^ 1 is free here (its last
+                // readers, chunk c - 1's scores, are past the barrier; the
+                // shared tile reads only its V half), so chunk c + 1's K moves
+                // in now and chunk c + 3's K is requested before the shared
+                // tile's work rather than after it
+                L &ldn = st == 0 ? ld1 : ld0;
+                if (i + 1 < nch) ldn.stage_k(ws_lds + (st ^ 1) * St::ELEMS, q);
+                ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
+            }
             if (NSH > 0 && i < nch) {
                 if (i > 0) shared_pv(ic<st ^ 1>{});
                 // scores of key tile q of chunk c for the shared tiles
@@ -564,11 +585,16 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                 if (lane == 0) ws_shflag[st][q] = flag;
             }
             // dequantise chunk c + 1 (raw bytes of parity st ^ 1) into stage
-            // st ^ 1, then request chunk c + 3 into the same registers
+            // st ^ 1, then request chunk c + 3 into the same registers (F16:
+            // the V half; its K half went at the top of the step)
             _Float16 *ks_n = ws_lds + (st ^ 1) * St::ELEMS;
             auto next = [&](L &ldn) {
-                if (i + 1 < nch) deq(ldn, ks_n);
-                ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
+                if constexpr (KVT == TV_KV_F16) {
+                    if (i + 1 < nch) ldn.stage_v(ks_n);
+                } else {
+                    if (i + 1 < nch) deq(ldn, ks_n);
+                    ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
+                }
                 ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
             };
             if constexpr (st == 0)
