@@ -420,9 +420,11 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             else
                 return 0;
         }();
-        auto deq = [&](const L &ld, _Float16 *stg) {
+        // the K and V halves of a chunk into stage `stg` (Q4_0 dequantised,
+        // F16 moved)
+        auto deq_k = [&](const L &ld, _Float16 *stg) {
             if constexpr (KVT == TV_KV_F16) {
-                ld.stage(stg, q);
+                ld.stage_k(stg, q);
             } else {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
@@ -430,6 +432,12 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
                     const h8 o = ld.k_values(j, magic, b, g);
                     *(h8 *)(stg + ksto + (j >> 2) * St::KFRAG + 128 * (j & 3)) = o;
                 }
+            }
+        };
+        auto deq_v = [&](const L &ld, _Float16 *stg) {
+            if constexpr (KVT == TV_KV_F16) {
+                ld.stage_v(stg);
+            } else {
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc) {
                     h2 vals[2][4];
@@ -447,7 +455,8 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             }
         };
         // chunk c_begin into stage 0; its raw registers then take chunk c_begin + 2
-        deq(ld0, ws_lds);
+        deq_k(ld0, ws_lds);
+        deq_v(ld0, ws_lds);
         ld0.load_k_ws(chunk_row<false>(a, c_begin + 2), 2 < nch);
         ld0.load_v(chunk_row<false>(a, c_begin + 2), 2 < nch);
 
@@ -525,14 +534,14 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
         auto body = [&](auto stc, int i) {
             constexpr int st = decltype(stc)::value;
             __syncthreads();
-            if constexpr (KVT == TV_KV_F16) {
-                // F16: the K half of stage st ^ 1 is free here (its last
-                // readers, chunk c - 1's scores, are past the barrier; the
-                // shared tile reads only its V half), so chunk c + 1's K moves
-                // in now and chunk c + 3's K is requested before the shared
-                // tile's work rather than after it
+            {
+                // the K half of stage st ^ 1 is free here (its last readers,
+                // chunk c - 1's scores, are past the barrier; the shared tile
+                // reads only its V half), so chunk c + 1's K moves in now and
+                // chunk c + 3's K is requested before the shared tile's work
+                // rather than after it
                 L &ldn = st == 0 ? ld1 : ld0;
-                if (i + 1 < nch) ldn.stage_k(ws_lds + (st ^ 1) * St::ELEMS, q);
+                if (i + 1 < nch) deq_k(ldn, ws_lds + (st ^ 1) * St::ELEMS);
                 ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
             }
             if (NSH > 0 && i < nch) {
@@ -589,12 +598,7 @@ __device__ __forceinline__ void ws_split(const SplitArgs &a, const SplitPtrs &p,
             // the V half; its K half went at the top of the step)
             _Float16 *ks_n = ws_lds + (st ^ 1) * St::ELEMS;
             auto next = [&](L &ldn) {
-                if constexpr (KVT == TV_KV_F16) {
-                    if (i + 1 < nch) ldn.stage_v(ks_n);
-                } else {
-                    if (i + 1 < nch) deq(ldn, ks_n);
-                    ldn.load_k_ws(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
-                }
+                if (i + 1 < nch) deq_v(ldn, ks_n);
                 ldn.load_v(chunk_row<false>(a, c_begin + i + 3), i + 3 < nch);
             };
             if constexpr (st == 0)
